@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped int4-dequant MoE layer on one MI355X.
+
+One step = one moe_layer_forward call over T=2048 tokens of the
+Qwen3.6-35B-A3B-shaped layer (d=2048, f=512, E=256 routed experts, top-8, one
+shared expert, int4 groupwise-affine weights, 64 per group) with every input
+already resident in HBM: top-k routing, scan/scatter/block map, the gate/up
+grouped GEMM with SwiGLU and the down grouped GEMM with the weighted combine.
+
+Prints one JSON line: tokens/s (value), the roofline of the dominant kernel
+measured with HIP events recorded on the layer's stream inside the timed
+region, the T=1 decode bandwidth, and the CPU oracle timed on a bounded
+sample of the same workload (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E peak
+METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cpu-tokens", type=int, default=48, help="tokens in the CPU oracle sample (0: skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_int4_dequant_amd as moe
+    from grouped_int4_dequant_amd import binding as B
+    from synth import moe_inputs as S
+
+    moe.load()
+    dev = torch.device("cuda", 0)
+    cfg = S.CONFIGS[2]
+    sh, T = cfg.shape, cfg.T
+    p = S.make_problem(2)
+    layer = moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, p.layer, device=dev)
+    x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    lg = torch.from_numpy(p.logits).to(dev)
+    y = torch.empty((T, sh.d), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(moe.workspace_bytes(T, layer), dev)
+    stream = torch.cuda.current_stream()
+
+    lib = B.load()
+    lib.moe_layer_forward_timed.argtypes = [
+        B.ctypes.POINTER(B.MoeLayerT), B._P, B._P, B._I32, B._P, B._P, B._P, B.ctypes.c_size_t, B._P,
+        B.ctypes.POINTER(B._P)]
+    lib.moe_layer_forward_timed.restype = B.ctypes.c_int
+
+    def make_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)  # creates the underlying hipEvent
+        return evs
+
+    def timed_call(evs):
+        arr = (B._P * 5)(*[e.cuda_event for e in evs])
+        st = lib.moe_layer_forward_timed(B.ctypes.byref(layer.c), x.data_ptr(), lg.data_ptr(), T,
+                                         y.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                         stream.cuda_stream, arr)
+        if st != 0:
+            raise RuntimeError(moe.status_string(st))
+
+    for _ in range(args.warmup):
+        moe.layer_forward(layer, x, lg, y=y, ws=ws)
+    step_events = [make_events(5) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for evs in step_events:
+        timed_call(evs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    stages = ["topk", "scan", "gate_up", "down"]
+    dur = {s: float(np.mean([evs[i].elapsed_time(evs[i + 1]) for evs in step_events]))
+           for i, s in enumerate(stages)}  # ms
+    gpu_ms = float(np.mean([evs[0].elapsed_time(evs[4]) for evs in step_events]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    flops_tok_gu = 2 * 2 * sh.d * (sh.k * sh.f + sh.f_sh)  # gate/up: 2 flops x 2f x d per row
+    flops_tok_dn = 2 * sh.d * (sh.k * sh.f + sh.f_sh)
+    kern_flops = {"gate_up": flops_tok_gu * T, "down": flops_tok_dn * T}
+    dom = max(kern_flops, key=lambda s: dur[s])
+    achieved = kern_flops[dom] / (dur[dom] * 1e-3) / 1e12
+    layer_tflops = (flops_tok_gu + flops_tok_dn) * T / (gpu_ms * 1e-3) / 1e12
+    touched_bytes = (sh.E + 1) * S.bytes_per_expert(sh)
+
+    out = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_prefill", "T": T, "d": sh.d, "f": sh.f, "E": sh.E, "k": sh.k,
+                   "f_sh": sh.f_sh, "weights": "int4 groupwise-affine g=64 bf16 scale+bias",
+                   "inputs": "seeded synthetic (config 2 recipe)"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None},
+        "stages_us": {s: dur[s] * 1e3 for s in stages},
+        "layer": {"gpu_us": gpu_ms * 1e3, "useful_tflops": layer_tflops,
+                  "mfma_frac": layer_tflops / MFMA_PEAK_TFLOPS,
+                  "weight_gbps": touched_bytes / (gpu_ms * 1e-3) / 1e9},
+    }
+
+    if args.decode_steps > 0:
+        out["decode_t1"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events)
+    del layer, x, lg, y, ws
+    torch.cuda.empty_cache()
+    if args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
+    """T=1 steps with fresh logits and x, rotating over 4 device copies of the
+    weights (about 1.8 GB, larger than the last-level cache) so repeated
+    experts are not served from cache. Bytes per step are exact: the packed
+    codes, scales and biases of the distinct experts touched plus the shared
+    expert."""
+    cfg = S.CONFIGS[4]
+    sh = cfg.shape
+    steps = list(S.decode_steps(1, steps=nsteps + 20))
+    layers = [moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, steps[0].layer, device=dev)
+              for _ in range(4)]
+    xs = [torch.from_numpy(s.x.view(np.int16)).view(torch.bfloat16).to(dev) for s in steps]
+    lgs = [torch.from_numpy(s.logits).to(dev) for s in steps]
+    y = torch.empty((1, sh.d), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(moe.workspace_bytes(1, layers[0]), dev)
+    per_expert = S.bytes_per_expert(sh)
+    nbytes = []
+    for s in steps:
+        touched = len(np.unique(np.argsort(-s.logits[0], kind="stable")[:sh.k]))
+        nbytes.append((touched + 1) * per_expert)
+    for i in range(20):
+        moe.layer_forward(layers[i % 4], xs[i], lgs[i], y=y, ws=ws)
+    evs_all = [make_events(5) for _ in range(nsteps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        L = layers[i % 4]
+        arr = (B._P * 5)(*[e.cuda_event for e in evs_all[i]])
+        st = lib.moe_layer_forward_timed(B.ctypes.byref(L.c), xs[20 + i].data_ptr(), lgs[20 + i].data_ptr(), 1,
+                                         y.data_ptr(), None, ws.data_ptr(), ws.numel(), stream.cuda_stream, arr)
+        assert st == 0
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / nsteps
+    gpu = float(np.mean([e[0].elapsed_time(e[4]) for e in evs_all])) * 1e-3
+    gemm = float(np.mean([e[2].elapsed_time(e[4]) for e in evs_all])) * 1e-3
+    b = float(np.mean(nbytes[20:]))
+    return {"T": 1, "steps": nsteps, "bytes_per_step": b,
+            "gpu_us_per_step": gpu * 1e6, "wall_us_per_step": wall * 1e6,
+            "gbps_gpu": b / gpu / 1e9, "gbps_gemm_kernels": b / gemm / 1e9,
+            "frac_hbm_gpu": b / gpu / 1e9 / HBM_PEAK_GBPS, "peak_gbps": HBM_PEAK_GBPS}
+
+
+def cpu_baseline(p, ntok):
+    """The fp64 oracle as it stands, on the first ntok tokens of the same
+    workload (their routed experts and the shared expert, dequantisation
+    included), scaled to tokens/s."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    tok = np.arange(ntok)
+    t0 = time.perf_counter()
+    O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ntok} of {p.T} tokens of the T={p.T} workload, fp64 numpy oracle "
+                      f"including dequantisation of every expert they touch ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,250 @@
+"""ctypes binding of libmoe_int4.so (the C ABI in include/moe_int4.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library. PyTorch supplies device memory and the current HIP stream. The
+module raises when the library is missing; there is no fallback path.
+
+Tensor formats:
+  bf16 values       torch.bfloat16 tensors (passed as uint16 bit patterns)
+  packed int4 codes torch.int32 tensors holding the uint32 words
+  logits, y         torch.float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+class MoeLayerT(ctypes.Structure):
+    _fields_ = [("d", _I32), ("f", _I32), ("E", _I32), ("k", _I32), ("f_sh", _I32),
+                ("gu_q", _P), ("gu_s", _P), ("gu_b", _P),
+                ("dn_q", _P), ("dn_s", _P), ("dn_b", _P),
+                ("sh_gu_q", _P), ("sh_gu_s", _P), ("sh_gu_b", _P),
+                ("sh_dn_q", _P), ("sh_dn_s", _P), ("sh_dn_b", _P)]
+
+
+class MoeRoutingT(ctypes.Structure):
+    _fields_ = [("topk_ids", _P), ("topk_w", _P), ("counts", _P), ("offsets", _P),
+                ("sorted_pair", _P), ("sorted_token", _P), ("pair_pos", _P),
+                ("block_map", _P), ("num_blocks", _P)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises FileNotFoundError when it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with grouped_int4_dequant_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.moe_max_blocks.argtypes = [_I32, _I32, _I32]
+        lib.moe_max_blocks.restype = _I32
+        lib.moe_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT)]
+        lib.moe_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_route_workspace_bytes.argtypes = [_I32, _I32]
+        lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_route.argtypes = [_P, _I32, _I32, _I32, ctypes.POINTER(MoeRoutingT), _P,
+                                  ctypes.c_size_t, _P]
+        lib.moe_route.restype = ctypes.c_int
+        lib.moe_grouped_gemm_int4.argtypes = [_P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _I32,
+                                              _P, _I32, _P]
+        lib.moe_grouped_gemm_int4.restype = ctypes.c_int
+        lib.moe_layer_forward.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
+                                          ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P]
+        lib.moe_layer_forward.restype = ctypes.c_int
+        lib.moe_prefill_chunked.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _I32, _P, _P,
+                                            ctypes.c_size_t, _P]
+        lib.moe_prefill_chunked.restype = ctypes.c_int
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise ValueError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class Layer:
+    """Device weights of one MoE layer plus the moe_layer_t that points at them."""
+
+    KEYS = ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b",
+            "sh_gu_q", "sh_gu_s", "sh_gu_b", "sh_dn_q", "sh_dn_s", "sh_dn_b")
+
+    def __init__(self, d: int, f: int, E: int, k: int, f_sh: int, tensors: Dict[str, torch.Tensor]):
+        self.d, self.f, self.E, self.k, self.f_sh = d, f, E, k, f_sh
+        self.tensors = dict(tensors)
+        shapes = {"gu_q": (E, 2 * f, d // 8), "gu_s": (E, 2 * f, d // 64), "gu_b": (E, 2 * f, d // 64),
+                  "dn_q": (E, d, f // 8), "dn_s": (E, d, f // 64), "dn_b": (E, d, f // 64),
+                  "sh_gu_q": (2 * f_sh, d // 8), "sh_gu_s": (2 * f_sh, d // 64),
+                  "sh_gu_b": (2 * f_sh, d // 64), "sh_dn_q": (d, f_sh // 8),
+                  "sh_dn_s": (d, f_sh // 64), "sh_dn_b": (d, f_sh // 64)}
+        ptrs = {}
+        for key in self.KEYS:
+            if key.startswith("sh_") and f_sh == 0:
+                ptrs[key] = None
+                continue
+            t = self.tensors[key]
+            _need(t, key, torch.int32 if key.endswith("_q") else torch.bfloat16, shapes[key])
+            ptrs[key] = t.data_ptr()
+        self.c = MoeLayerT(d, f, E, k, f_sh, *[ptrs[k_] for k_ in self.KEYS])
+
+    @classmethod
+    def from_numpy(cls, d, f, E, k, f_sh, arrays, device="cuda"):
+        """Upload generator arrays (uint32 codes, uint16 bf16 bits) to the GPU."""
+        import numpy as np
+        ts = {}
+        for key, a in arrays.items():
+            if key.endswith("_q"):
+                ts[key] = torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device)
+            else:
+                ts[key] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        return cls(d, f, E, k, f_sh, ts)
+
+
+def max_blocks(T: int, E: int, k: int) -> int:
+    return int(load().moe_max_blocks(T, E, k))
+
+
+def workspace_bytes(T: int, layer: Layer) -> int:
+    return int(load().moe_workspace_bytes(T, ctypes.byref(layer.c)))
+
+
+def route_workspace_bytes(T: int, E: int) -> int:
+    return int(load().moe_route_workspace_bytes(T, E))
+
+
+def alloc_routing(T: int, E: int, k: int, device="cuda") -> Dict[str, torch.Tensor]:
+    mb = max_blocks(T, E, k)
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(topk_ids=torch.empty((T, k), **i32),
+                topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                sorted_pair=torch.empty(T * k, **i32), sorted_token=torch.empty(T * k, **i32),
+                pair_pos=torch.empty(T * k, **i32), block_map=torch.empty((mb, 3), **i32),
+                num_blocks=torch.empty(1, **i32))
+
+
+def _routing_struct(r: Dict[str, torch.Tensor]) -> MoeRoutingT:
+    for key, t in r.items():
+        _need(t, key, torch.float32 if key == "topk_w" else torch.int32)
+    return MoeRoutingT(*[r[k].data_ptr() for k in ("topk_ids", "topk_w", "counts", "offsets",
+                                                   "sorted_pair", "sorted_token", "pair_pos",
+                                                   "block_map", "num_blocks")])
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Workspace buffer (torch's caching allocator returns 256-byte aligned storage)."""
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def route(logits: torch.Tensor, k: int, out: Optional[Dict[str, torch.Tensor]] = None,
+          ws: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """moe_route: GPU top-k, gates, histogram, scan, stable scatter and block map."""
+    T, E = logits.shape
+    _need(logits, "logits", torch.float32)
+    out = alloc_routing(T, E, k, logits.device) if out is None else out
+    need = route_workspace_bytes(T, E)
+    ws = alloc_workspace(need, logits.device) if ws is None else ws
+    rs = _routing_struct(out)
+    _check(load().moe_route(logits.data_ptr(), T, E, k, ctypes.byref(rs), ws.data_ptr(),
+                            ws.numel(), _stream(stream)), "moe_route")
+    return out
+
+
+def grouped_gemm_int4(A: torch.Tensor, a_row: Optional[torch.Tensor], N: int, K: int,
+                      Wq: torch.Tensor, Ws: torch.Tensor, Wb: torch.Tensor,
+                      block_map: torch.Tensor, num_blocks: torch.Tensor, C: torch.Tensor,
+                      stream=None) -> torch.Tensor:
+    """moe_grouped_gemm_int4: C[p] = A[row(p)] @ W_e(p)^T for the rows of every block."""
+    _need(A, "A", torch.bfloat16)
+    _need(Wq, "Wq", torch.int32)
+    _need(Ws, "Ws", torch.bfloat16)
+    _need(Wb, "Wb", torch.bfloat16)
+    _need(block_map, "block_map", torch.int32)
+    _need(num_blocks, "num_blocks", torch.int32)
+    _need(C, "C", torch.float32)
+    if a_row is not None:
+        _need(a_row, "a_row", torch.int32)
+    _check(load().moe_grouped_gemm_int4(A.data_ptr(), A.shape[-1], _ptr(a_row), N, K,
+                                        Wq.data_ptr(), Ws.data_ptr(), Wb.data_ptr(),
+                                        block_map.data_ptr(), num_blocks.data_ptr(),
+                                        block_map.shape[0], C.data_ptr(), C.shape[-1],
+                                        _stream(stream)), "moe_grouped_gemm_int4")
+    return C
+
+
+def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
+                  y: Optional[torch.Tensor] = None,
+                  routing: Optional[Dict[str, torch.Tensor]] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_layer_forward: the whole layer for T tokens into fp32 y."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(logits, "logits", torch.float32, (T, layer.E))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load().moe_layer_forward(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                    y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
+                                    ws.data_ptr(), ws.numel(), _stream(stream)),
+           "moe_layer_forward")
+    return y
+
+
+def prefill_chunked(layer: Layer, x: torch.Tensor, logits: torch.Tensor, chunk: int = 2048,
+                    y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """moe_prefill_chunked: the layer over bounded chunks with one reused workspace."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(logits, "logits", torch.float32, (T, layer.E))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    ws = alloc_workspace(workspace_bytes(min(chunk, max(T, 1)), layer), x.device) if ws is None else ws
+    _check(load().moe_prefill_chunked(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                      chunk, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      _stream(stream)), "moe_prefill_chunked")
+    return y

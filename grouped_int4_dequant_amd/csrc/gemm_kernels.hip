@@ -1,0 +1,389 @@
+// Grouped GEMM over uneven expert groups with on-chip int4 dequantisation,
+// written for gfx950 (MI355X).
+//
+// The Lily pages rebuild the 4-bit groupwise-affine weights one tile at a time
+// inside the grouped GEMM, keep the rebuilt tile on chip and accumulate in
+// FP32, so the expanded weights never reach memory (Lily-EN "Prefill: Keep
+// Weights Packed, Keep Routing on the GPU"; Lily-ES "Precarga: mantenga los
+// pesos empaquetados, siga enrutando en la GPU", which also gives the group
+// of 64 weights sharing one bf16 scale and one bf16 bias and the 32-row
+// tiles). That design targeted Metal tensor ops on bf16; on gfx950 it becomes:
+//
+//   * Work unit: up to 128 rows (four 32-row blocks) of one expert x one
+//     N-slice of the weights. A workgroup is 4 waves; a wave owns 64 weight
+//     rows (output columns) as four 16-column MFMA blocks and every row of
+//     the unit, so each rebuilt weight feeds every row of the unit.
+//   * Weights go HBM -> VGPR with 128-bit loads, one step ahead of use, and
+//     are rebuilt in registers: v_and_or_b32 puts two codes into fp16 "1024+q"
+//     slots, v_pk_add_f16 removes 1032 exactly, v_pk_fma_f16 applies the group
+//     scale and bias: w = fp16(s*(q-8) + (b+8s)). Only registers hold the
+//     rebuilt tile; nothing expanded is written anywhere.
+//   * Activations (fp16, each 8-run stored as 0,4,1,5,2,6,3,7 to match the
+//     register order of the rebuilt codes) are gathered by row with 128-bit
+//     loads one step ahead and written to LDS, double buffered, XOR-swizzled
+//     so the 16 rows read by one MFMA operand fetch hit distinct banks.
+//   * v_mfma_f32_16x16x32_f16, fp32 accumulators in AGPRs. 16-row MFMA blocks
+//     let a partial 32-row block skip its empty half.
+//   * Epilogues: SwiGLU into fp16 h (gate/up projection); weighted combine
+//     into fp32 y with atomics (down projection); plain fp32 store
+//     (stand-alone grouped GEMM).
+//
+// K loop: the four 16-lane quarters of a wave split K into four contiguous
+// ranges; at step s quarter kq handles group kq*steps + s, so a lane reads 32
+// contiguous bytes of codes and one scale/bias per column per step. K is
+// padded to a multiple of 256 with zero weights.
+//
+// Pages cited (titles as published):
+//   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
+//            for Qwen3.6-35B-A3B on Apple Silicon" (insight.aitobox.com)
+//   Lily-ES  "Perplexity open sources Lily: un motor de inferencia ... para
+//            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
+
+#include "moe_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace moe {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = kThreads / 64;
+constexpr int kCB = 4;                            // 16-column MFMA blocks per wave
+constexpr int kRowBytes = 512;                    // one row of one K step: 4 quarters x 64 fp16
+constexpr int kBufBytes = kUnitRows * kRowBytes;  // one K step of a 128-row unit (64 KiB)
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+struct BStage {
+  u4 q[kCB][2];        // 8 code words (64 codes) per column block
+  uint32_t s[kCB];     // bf16 scale bits
+  uint32_t b[kCB];     // bf16 bias bits
+};
+
+// A VGPR holding a constant, so v_and_or_b32 can take the mask from a VGPR
+// and the fp16 magic from an SGPR (VOP3 on gfx9 takes no literal).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) {
+  return __uint_as_float(bits << 16);
+}
+
+// Workgroup barrier that first drains this wave's LDS operations. The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __half_as_ushort(__float2half_rn(v));
+}
+
+// Column position of logical column n in the permuted-run activation layout
+// (each run of 8 stored as 0,4,1,5,2,6,3,7).
+__device__ __forceinline__ int perm_col(int n) {
+  return (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
+}
+
+struct Unit {
+  int e, r0, nr;
+  int slice;
+};
+
+template <int MODE, bool AF16, int RB32>
+__device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
+                                         const int *s_arow, const int *s_tok, const float *s_gw) {
+  constexpr int kMaxRB = 2 * RB32;                          // 16-row MFMA blocks
+  constexpr int kInstA = (32 * RB32 / 2 + kWaves - 1) / kWaves;  // A slabs per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, kq = lane >> 4;
+  const int N = P.N, K = P.K, G = K >> 6, steps = (K + 255) >> 8;
+  const int nr = U.nr, nrb = (nr + 15) >> 4;
+
+  // columns (weight rows) of this wave
+  int ncol[kCB];
+  bool active;
+  if (MODE == kSwiGLU) {
+    const int f = N >> 1, ng = U.slice * 128 + wave * 32;
+    active = ng < f;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+      ncol[cb] = (cb < 2 ? ng + 16 * cb : f + ng + 16 * (cb - 2)) + c16;
+  } else {
+    const int n0 = U.slice * 256 + wave * 64;
+    active = n0 < N;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) ncol[cb] = n0 + 16 * cb + c16;
+  }
+  if (!active) {  // idle waves still issue in-bounds loads to keep counts uniform
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) ncol[cb] = c16;
+  }
+
+  const uint32_t *wq = P.Wq + (int64_t)U.e * P.wq_estride;
+  const uint16_t *wsc = P.Ws + (int64_t)U.e * P.ws_estride;
+  const uint16_t *wbi = P.Wb + (int64_t)U.e * P.ws_estride;
+  const int kw = K >> 3;
+
+  auto load_b = [&](BStage &st, int s) {
+    const int g = kq * steps + s;
+    const int gc = g < G ? g : 0;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const u4 *p = reinterpret_cast<const u4 *>(wq + (int64_t)ncol[cb] * kw + 8 * gc);
+      st.q[cb][0] = p[0];
+      st.q[cb][1] = p[1];
+      st.s[cb] = wsc[(int64_t)ncol[cb] * G + gc];
+      st.b[cb] = wbi[(int64_t)ncol[cb] * G + gc];
+    }
+  };
+
+  // A tile of step s -> LDS buffer, staged through registers. Slot (row r,
+  // 16-byte position p) of a buffer holds logical chunk p ^ (r & 15):
+  // quarter (chunk >> 3), 8-run (chunk & 7). One 1 KiB slab = rows 2i, 2i+1.
+  uint4 a_regs[kInstA];
+  auto load_a = [&](int s) {
+#pragma unroll
+    for (int ii = 0; ii < kInstA; ++ii) {
+      const int i = wave + kWaves * ii;
+      const int r = 2 * i + (lane >> 5);
+      const int ch = (lane & 31) ^ (r & 15);
+      const int g = (ch >> 3) * steps + s;
+      const int kel = g < G ? 64 * g + 8 * (ch & 7) : 0;
+      const int64_t row = s_arow[min(r, nr - 1)];
+      a_regs[ii] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.A) +
+                                                    row * P.lda + kel);
+    }
+  };
+  auto store_a = [&](int buf) {
+    uint8_t *dst0 = lds + buf * kBufBytes;
+#pragma unroll
+    for (int ii = 0; ii < kInstA; ++ii) {
+      const int i = wave + kWaves * ii;
+      uint4 o = a_regs[ii];
+      if (!AF16) {  // natural-order bf16 run -> permuted fp16 run
+        const uint4 v = o;
+        auto cvt = [](uint32_t lo_src, uint32_t hi_src, bool upper) {
+          const uint32_t l = upper ? (lo_src & 0xFFFF0000u) : (lo_src << 16);
+          const uint32_t h = upper ? (hi_src & 0xFFFF0000u) : (hi_src << 16);
+          return (uint32_t)f32_to_f16_bits(__uint_as_float(l)) |
+                 ((uint32_t)f32_to_f16_bits(__uint_as_float(h)) << 16);
+        };
+        o.x = cvt(v.x, v.z, false);  // (e0, e4)
+        o.y = cvt(v.x, v.z, true);   // (e1, e5)
+        o.z = cvt(v.y, v.w, false);  // (e2, e6)
+        o.w = cvt(v.y, v.w, true);   // (e3, e7)
+      }
+      *reinterpret_cast<uint4 *>(dst0 + i * 1024 + 16 * lane) = o;
+    }
+  };
+
+  f4 acc[kMaxRB][kCB];
+#pragma unroll
+  for (int rb = 0; rb < kMaxRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t m_lo = vgpr_const(0x000F000Fu), m_hi = vgpr_const(0x00F000F0u);
+  const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
+
+  auto compute = [&](const BStage &st, int s, int buf) {
+    const bool gvalid = kq * steps + s < G;
+    h2 s1[kCB], s16[kCB], cc[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      float sf = bf16_bits_to_float(st.s[cb]), bf = bf16_bits_to_float(st.b[cb]);
+      if (!gvalid) sf = bf = 0.f;
+      const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f), ch = (_Float16)(bf + 8.f * sf);
+      s1[cb] = h2{sh, sh};
+      s16[cb] = h2{sh16, sh16};
+      cc[cb] = h2{ch, ch};
+    }
+    const h2 off1 = h2{(_Float16)-1032.f, (_Float16)-1032.f};
+    const h2 off16 = h2{(_Float16)-1152.f, (_Float16)-1152.f};
+    const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h8 bfrag[kCB];
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        const uint32_t w = j < 4 ? st.q[cb][0][j] : st.q[cb][1][j - 4];
+        const uint32_t w8 = w >> 8;
+        // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
+        const h2 t0 = __builtin_bit_cast(h2, (w & m_lo) | magic) + off1;
+        const h2 t1 = __builtin_bit_cast(h2, (w & m_hi) | magic) + off16;
+        const h2 t2 = __builtin_bit_cast(h2, (w8 & m_lo) | magic) + off1;
+        const h2 t3 = __builtin_bit_cast(h2, (w8 & m_hi) | magic) + off16;
+        const h2 w0 = __builtin_elementwise_fma(t0, s1[cb], cc[cb]);
+        const h2 w1 = __builtin_elementwise_fma(t1, s16[cb], cc[cb]);
+        const h2 w2 = __builtin_elementwise_fma(t2, s1[cb], cc[cb]);
+        const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
+        bfrag[cb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      }
+      const int aoff = 16 * ((8 * kq + j) ^ c16);
+#pragma unroll
+      for (int rb = 0; rb < kMaxRB; ++rb) {
+        if (rb < nrb) {
+          const h8 a = *reinterpret_cast<const h8 *>(abuf + rb * 16 * kRowBytes + aoff);
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bfrag[cb], acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One K step: the barrier publishes A(s) (written to LDS during the
+  // previous step) and frees the other buffer; A(s+1) and B(s+1) are
+  // requested, step s is computed, then A(s+1) is written to LDS. Loads are
+  // issued unconditionally (clamped to the last step) so every step has the
+  // same number in flight and the compiler's wait counts stay exact.
+  auto body = [&](int s, const BStage &cur, BStage &nxt) {
+    lds_barrier();
+    const int sn = min(s + 1, steps - 1);
+    load_a(sn);
+    load_b(nxt, sn);
+    if (active && s < steps) compute(cur, s, s & 1);
+    store_a((s + 1) & 1);
+  };
+
+  BStage b0, b1;
+  load_a(0);
+  load_b(b0, 0);
+  store_a(0);
+  for (int s = 0; s < steps; s += 2) {
+    body(s, b0, b1);
+    body(s + 1, b1, b0);
+  }
+
+  if (!active) return;
+  // ------------------------------------------------------------- epilogue
+  // accumulator element i of lane (c16, kq) in block (rb, cb) is row
+  // 16*rb + 4*kq + i, column 16*cb + c16 of the wave's tile
+  if (MODE == kSwiGLU) {
+    const int ng = U.slice * 128 + wave * 32;
+#pragma unroll
+    for (int rb = 0; rb < kMaxRB; ++rb) {
+      if (rb >= nrb) break;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int col = perm_col(ng + 16 * cb + c16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rb + 4 * kq + i;
+          if (r < nr) {
+            const float g = acc[rb][cb][i], u = acc[rb][cb + 2][i];
+            const float h = g / (1.f + __expf(-g)) * u;
+            P.H[(int64_t)(U.r0 + r) * P.ldh + col] = f32_to_f16_bits(h);
+          }
+        }
+      }
+    }
+  } else if (MODE == kCombine) {
+    const int n0 = U.slice * 256 + wave * 64;
+#pragma unroll
+    for (int rb = 0; rb < kMaxRB; ++rb) {
+      if (rb >= nrb) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * kq + i;
+        if (r < nr) {
+          float *yrow = P.Y + (int64_t)s_tok[r] * P.ldy + n0 + c16;
+          const float w = s_gw[r];
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) unsafeAtomicAdd(yrow + 16 * cb, w * acc[rb][cb][i]);
+        }
+      }
+    }
+  } else {
+    const int n0 = U.slice * 256 + wave * 64;
+#pragma unroll
+    for (int rb = 0; rb < kMaxRB; ++rb) {
+      if (rb >= nrb) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * kq + i;
+        if (r < nr) {
+          float *crow = P.C + (int64_t)(U.r0 + r) * P.ldc + n0 + c16;
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) crow[16 * cb] = acc[rb][cb][i];
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, bool AF16>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
+  __shared__ int s_arow[kUnitRows];
+  __shared__ int s_tok[kUnitRows];
+  __shared__ float s_gw[kUnitRows];
+
+  const int b = blockIdx.x;
+  const bool second = args.nprob > 1 && b >= args.prob[1].wg_begin;
+  const GemmProblem P = second ? args.prob[1] : args.prob[0];
+  // Workgroup i runs on XCD i % 8. Consecutive groups of 8 workgroups take 8
+  // units (one per XCD); the N-slices of one unit stay on one XCD, so its
+  // gathered activation rows are fetched into that XCD's L2 once.
+  const int lb = b - P.wg_begin;
+  const int slot = lb >> 3;
+  Unit U;
+  const int unit = (slot / P.nslices) * 8 + (lb & 7);
+  U.slice = slot % P.nslices;
+  if (P.units) {
+    if (unit >= *P.num_units) return;
+    const int32_t *u = P.units + 3 * (int64_t)unit;
+    U.e = u[0];
+    U.r0 = u[1];
+    U.nr = u[2];
+  } else {
+    U.e = 0;
+    U.r0 = unit * kUnitRows;
+    U.nr = min(kUnitRows, P.implicit_rows - U.r0);
+    if (U.nr <= 0) return;
+  }
+
+  for (int r = threadIdx.x; r < kUnitRows; r += kThreads) {
+    const int p = U.r0 + min(r, U.nr - 1);
+    s_arow[r] = P.a_row ? P.a_row[p] : p;
+    if (MODE == kCombine) {
+      s_tok[r] = P.row_token ? P.row_token[p] : p;
+      s_gw[r] = P.pair_w ? P.pair_w[P.row_pair[p]] : 1.f;
+    }
+  }
+  __syncthreads();
+
+  switch ((U.nr + 31) >> 5) {
+    case 1: run_unit<MODE, AF16, 1>(P, U, lds, s_arow, s_tok, s_gw); break;
+    case 2: run_unit<MODE, AF16, 2>(P, U, lds, s_arow, s_tok, s_gw); break;
+    case 3: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, s_tok, s_gw); break;
+    default: run_unit<MODE, AF16, 4>(P, U, lds, s_arow, s_tok, s_gw); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s) {
+  const dim3 grid(a.total_wg), block(kThreads);
+  if (a.total_wg == 0) return hipSuccess;
+  if (a_f16) {
+    switch (mode) {
+      case kSwiGLU: hipLaunchKernelGGL((gemm_kernel<kSwiGLU, true>), grid, block, 0, s, a); break;
+      case kCombine: hipLaunchKernelGGL((gemm_kernel<kCombine, true>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_kernel<kStoreC, true>), grid, block, 0, s, a); break;
+    }
+  } else {
+    // bf16 activations: stand-alone GEMM over block-map entries (<= 32 rows)
+    hipLaunchKernelGGL((gemm_kernel<kStoreC, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

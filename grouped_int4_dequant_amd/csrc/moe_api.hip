@@ -1,0 +1,359 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and
+// the launch sequence. Every check runs on the host before anything is
+// enqueued; nothing here reads device memory or synchronises.
+//
+// Pages cited (titles as published):
+//   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
+//            for Qwen3.6-35B-A3B on Apple Silicon" (insight.aitobox.com)
+//   Lily-ES  "Perplexity open sources Lily: un motor de inferencia ... para
+//            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
+
+#include "moe_internal.h"
+
+#include <algorithm>
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;  // scan cost grows with (T/64)^2
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char *base;
+  size_t off = 0;
+  template <typename T>
+  T *take(size_t count) {
+    off = (size_t)round_up((int64_t)off, kAlign);
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+int64_t max_units_routed(int T, int k, int E) { return ceil_div((int64_t)T * k, kUnitRows) + E; }
+
+int check_layer(const moe_layer_t *L) {
+  if (!L) return MOE_EINVAL;
+  if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->f_sh < 0) return MOE_EINVAL;
+  if (L->k > L->E) return MOE_EINVAL;
+  if (L->E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+  if (L->d % 64 || L->f % 64 || L->f_sh % 64) return MOE_EUNSUPPORTED;
+  const void *req[] = {L->gu_q, L->gu_s, L->gu_b, L->dn_q, L->dn_s, L->dn_b};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+  if (L->f_sh > 0) {
+    const void *sh[] = {L->sh_gu_q, L->sh_gu_s, L->sh_gu_b, L->sh_dn_q, L->sh_dn_s, L->sh_dn_b};
+    for (const void *p : sh)
+      if (!p || !aligned16(p)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+int check_routing(const moe_routing_t *r) {
+  if (!r) return MOE_EINVAL;
+  const void *req[] = {r->topk_ids, r->topk_w, r->counts, r->offsets, r->sorted_pair,
+                       r->sorted_token, r->pair_pos, r->block_map, r->num_blocks};
+  for (const void *p : req)
+    if (!p) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+struct Workspace {
+  uint64_t *masks;
+  moe_routing_t rt;
+  int32_t *units, *num_units;
+  uint16_t *x16, *h, *h_sh;
+};
+
+// Layout of the layer workspace for T tokens (base == nullptr: size only).
+size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
+  Carver c{base};
+  const int E = L->E, k = L->k;
+  const int64_t C = ceil_div(T, kSubChunk);
+  const int64_t tk = (int64_t)T * k;
+  Workspace o;
+  o.masks = c.take<uint64_t>(C * E);
+  o.rt.topk_ids = c.take<int32_t>(tk);
+  o.rt.topk_w = c.take<float>(tk);
+  o.rt.counts = c.take<int32_t>(E);
+  o.rt.offsets = c.take<int32_t>(E + 1);
+  o.rt.sorted_pair = c.take<int32_t>(tk);
+  o.rt.sorted_token = c.take<int32_t>(tk);
+  o.rt.pair_pos = c.take<int32_t>(tk);
+  o.rt.block_map = c.take<int32_t>(3 * (size_t)moe_max_blocks(T, E, k));
+  o.rt.num_blocks = c.take<int32_t>(1);
+  o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E));
+  o.num_units = c.take<int32_t>(1);
+  o.x16 = c.take<uint16_t>((size_t)T * L->d);
+  o.h = c.take<uint16_t>((size_t)tk * L->f);
+  o.h_sh = c.take<uint16_t>((size_t)T * L->f_sh);
+  if (w) *w = o;
+  return (size_t)round_up((int64_t)c.off, kAlign);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+int record(hipEvent_t *ev, int i, hipStream_t s);
+
+int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
+                  uint64_t *masks, int32_t *units, int32_t *num_units, const uint16_t *x,
+                  uint16_t *x16, float *y, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
+  TopkArgs ta{};
+  ta.logits = logits;
+  ta.T = T;
+  ta.E = E;
+  ta.k = k;
+  ta.topk_ids = rt.topk_ids;
+  ta.topk_w = rt.topk_w;
+  ta.masks = masks;
+  ta.n_route_blocks = (int)ceil_div(T, kSubChunk);
+  ta.x = x;
+  ta.x16 = x16;
+  ta.y = y;
+  ta.d = d;
+  int n_aux = 0;
+  if (x16) n_aux = (int)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div((int64_t)T * d / 8, 4 * kThreads)));
+  hipError_t err = launch_topk(ta, n_aux, s);
+  if (err != hipSuccess) return MOE_EHIP;
+  if (record(ev, 1, s) != MOE_OK) return MOE_EHIP;
+
+  ScanArgs sa{};
+  sa.T = T;
+  sa.E = E;
+  sa.k = k;
+  sa.topk_ids = rt.topk_ids;
+  sa.masks = masks;
+  sa.counts = rt.counts;
+  sa.offsets = rt.offsets;
+  sa.sorted_pair = rt.sorted_pair;
+  sa.sorted_token = rt.sorted_token;
+  sa.pair_pos = rt.pair_pos;
+  sa.block_map = rt.block_map;
+  sa.num_blocks = rt.num_blocks;
+  sa.max_blocks = moe_max_blocks(T, E, k);
+  sa.units = units;
+  sa.num_units = num_units;
+  sa.max_units = units ? (int)max_units_routed(T, k, E) : 0;
+  int st = hip_status(launch_scan(sa, s));
+  if (st == MOE_OK) st = record(ev, 2, s);
+  return st;
+}
+
+// Workgroups of one grouped problem: units rounded up to a multiple of 8 (one
+// unit per XCD per round) times the N-slices.
+int problem_wgs(int64_t max_units, int nslices) { return (int)(round_up(max_units, 8) * nslices); }
+
+int record(hipEvent_t *ev, int i, hipStream_t s) {
+  return ev ? hip_status(hipEventRecord(ev[i], s)) : MOE_OK;
+}
+
+int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
+                const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
+                hipEvent_t *ev = nullptr) {
+  const size_t need = carve_layer(T, L, nullptr, nullptr);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  Workspace w;
+  carve_layer(T, L, static_cast<char *>(ws), &w);
+  const moe_routing_t &rt = routing ? *routing : w.rt;
+  const int d = L->d, f = L->f, E = L->E, k = L->k, fs = L->f_sh;
+
+  int st = record(ev, 0, s);
+  if (st != MOE_OK) return st;
+  st = enqueue_route(logits, T, E, k, rt, w.masks, w.units, w.num_units, x, w.x16, y, d, s, ev);
+  if (st != MOE_OK) return st;
+
+  // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
+  GemmArgs g1{};
+  int nwg = 0, np = 0;
+  if (fs > 0) {
+    GemmProblem &p = g1.prob[np++];
+    p.A = w.x16; p.lda = d; p.a_row = nullptr;
+    p.Wq = L->sh_gu_q; p.Ws = L->sh_gu_s; p.Wb = L->sh_gu_b;
+    p.wq_estride = 0; p.ws_estride = 0;
+    p.N = 2 * fs; p.K = d;
+    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
+    p.nslices = (int)ceil_div(fs, 128);
+    p.wg_begin = nwg;
+    p.H = w.h_sh; p.ldh = fs;
+    nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
+  }
+  {
+    GemmProblem &p = g1.prob[np++];
+    p.A = w.x16; p.lda = d; p.a_row = rt.sorted_token;
+    p.Wq = L->gu_q; p.Ws = L->gu_s; p.Wb = L->gu_b;
+    p.wq_estride = (int64_t)2 * f * (d / 8); p.ws_estride = (int64_t)2 * f * (d / 64);
+    p.N = 2 * f; p.K = d;
+    p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
+    p.nslices = (int)ceil_div(f, 128);
+    p.wg_begin = nwg;
+    p.H = w.h; p.ldh = f;
+    nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
+  }
+  g1.nprob = np;
+  g1.total_wg = nwg;
+  st = hip_status(launch_gemm(g1, kSwiGLU, true, s));
+  if (st == MOE_OK) st = record(ev, 3, s);
+  if (st != MOE_OK) return st;
+
+  // down projection + weighted combine into y (zeroed by the routing kernel)
+  GemmArgs g2{};
+  nwg = 0;
+  np = 0;
+  if (fs > 0) {
+    GemmProblem &p = g2.prob[np++];
+    p.A = w.h_sh; p.lda = fs; p.a_row = nullptr;
+    p.Wq = L->sh_dn_q; p.Ws = L->sh_dn_s; p.Wb = L->sh_dn_b;
+    p.wq_estride = 0; p.ws_estride = 0;
+    p.N = d; p.K = fs;
+    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
+    p.nslices = (int)ceil_div(d, 256);
+    p.wg_begin = nwg;
+    p.Y = y; p.ldy = d; p.row_token = nullptr; p.row_pair = nullptr; p.pair_w = nullptr;
+    nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
+  }
+  {
+    GemmProblem &p = g2.prob[np++];
+    p.A = w.h; p.lda = f; p.a_row = nullptr;
+    p.Wq = L->dn_q; p.Ws = L->dn_s; p.Wb = L->dn_b;
+    p.wq_estride = (int64_t)d * (f / 8); p.ws_estride = (int64_t)d * (f / 64);
+    p.N = d; p.K = f;
+    p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
+    p.nslices = (int)ceil_div(d, 256);
+    p.wg_begin = nwg;
+    p.Y = y; p.ldy = d;
+    p.row_token = rt.sorted_token; p.row_pair = rt.sorted_pair; p.pair_w = rt.topk_w;
+    nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
+  }
+  g2.nprob = np;
+  g2.total_wg = nwg;
+  st = hip_status(launch_gemm(g2, kCombine, true, s));
+  if (st == MOE_OK) st = record(ev, 4, s);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E <= 0 || k <= 0) return 0;
+  return (int32_t)(ceil_div((int64_t)T * k, MOE_BLOCK_ROWS) + E);
+}
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 0 || E <= 0 || E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return 0;
+  return (size_t)round_up(ceil_div(T, kSubChunk) * E * (int64_t)sizeof(uint64_t), kAlign) + kAlign;
+}
+
+size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {
+  if (!L || T < 0 || T > kMaxRouteTokens) return 0;
+  if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->k > L->E || L->f_sh < 0) return 0;
+  if (L->E > MOE_MAX_EXPERTS || L->d % 64 || L->f % 64 || L->f_sh % 64) return 0;
+  return carve_layer(T, L, nullptr, nullptr);
+}
+
+int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_routing_t *out,
+              void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (check_routing(out) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!logits || !ws) return MOE_EINVAL;
+  if (ws_bytes < moe_route_workspace_bytes(T, E)) return MOE_EWORKSPACE;
+  char *base = reinterpret_cast<char *>(round_up((int64_t)(uintptr_t)ws, kAlign));
+  return enqueue_route(logits, T, E, k, *out, reinterpret_cast<uint64_t *>(base), nullptr, nullptr,
+                       nullptr, nullptr, nullptr, 0, stream);
+}
+
+int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, int32_t N,
+                          int32_t K, const uint32_t *Wq, const uint16_t *Ws, const uint16_t *Wb,
+                          const int32_t *block_map, const int32_t *num_blocks, int32_t max_blocks,
+                          float *C, int32_t ldc, hipStream_t stream) {
+  if (!A || !Wq || !Ws || !Wb || !block_map || !num_blocks || !C) return MOE_EINVAL;
+  if (N <= 0 || K <= 0 || max_blocks < 0 || lda < K || ldc < N) return MOE_EINVAL;
+  if (N % 64 || K % 64) return MOE_EUNSUPPORTED;
+  if (!aligned16(A) || lda % 8 || !aligned16(Wq) || !aligned16(Ws) || !aligned16(Wb))
+    return MOE_EINVAL;
+  if (max_blocks == 0) return MOE_OK;
+  GemmArgs g{};
+  GemmProblem &p = g.prob[0];
+  p.A = A; p.lda = lda; p.a_row = a_row;
+  p.Wq = Wq; p.Ws = Ws; p.Wb = Wb;
+  p.wq_estride = (int64_t)N * (K / 8); p.ws_estride = (int64_t)N * (K / 64);
+  p.N = N; p.K = K;
+  p.units = block_map; p.num_units = num_blocks; p.implicit_rows = 0;
+  p.nslices = (int)ceil_div(N, 256);
+  p.wg_begin = 0;
+  p.C = C; p.ldc = ldc;
+  g.nprob = 1;
+  g.total_wg = problem_wgs(max_blocks, p.nslices);
+  return hip_status(launch_gemm(g, kStoreC, false, stream));
+}
+
+int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                      float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float *logits,
+                            int32_t T, float *y, const moe_routing_t *routing, void *ws,
+                            size_t ws_bytes, hipStream_t stream, hipEvent_t *events) {
+  if (!events) return MOE_EINVAL;
+  for (int i = 0; i < 5; ++i)
+    if (!events[i]) return MOE_EINVAL;
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream, events);
+}
+
+int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                        int32_t chunk, float *y, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0 || chunk < 1) return MOE_EINVAL;
+  if (chunk > kMaxRouteTokens || T > MOE_MAX_TOKENS) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  const int32_t c0 = std::min(chunk, T);
+  if (ws_bytes < moe_workspace_bytes(c0, L)) return MOE_EWORKSPACE;
+  for (int32_t t0 = 0; t0 < T; t0 += chunk) {
+    const int32_t n = std::min(chunk, T - t0);
+    st = forward_one(L, x + (int64_t)t0 * L->d, logits + (int64_t)t0 * L->E, n,
+                     y + (int64_t)t0 * L->d, nullptr, ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, bad size, k > E)";
+    case MOE_EUNSUPPORTED: return "unsupported shape (d, f, f_sh not multiples of 64; E > 1024; too many tokens)";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

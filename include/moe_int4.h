@@ -1,0 +1,209 @@
+/*
+ * moe_int4.h - C ABI of the grouped int4-dequant Mixture-of-Experts layer for
+ * AMD MI355X (gfx950).
+ *
+ * The layer is the prefill MoE block the Lily pages describe for
+ * Qwen3.6-35B-A3B: a router picks k of E experts per token plus one shared
+ * expert that sees every token; routing (histogram, prefix scan, scatter,
+ * block map) stays on the GPU with no host synchronisation; a grouped GEMM
+ * streams 4-bit groupwise-affine weights and dequantises them on chip, one
+ * tile at a time, accumulating in FP32 so the expanded weights never reach
+ * device memory; the expert outputs are combined with the router weights.
+ *
+ * Pages cited (titles as published):
+ *   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine for
+ *            Qwen3.6-35B-A3B on Apple Silicon" (insight.aitobox.com), sections
+ *            "Three Workload Shapes", "Prefill: Keep Weights Packed, Keep
+ *            Routing on the GPU", "Decode: Minimize Bytes Moved Per Token".
+ *   Lily-ES  "Perplexity open sources Lily: un motor de inferencia ... para
+ *            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es), sections
+ *            "Precarga: mantenga los pesos empaquetados, siga enrutando en la
+ *            GPU" and "Decodificar: minimizar los bytes movidos por token".
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller, unless stated. The
+ *     library never allocates, frees or retains them past the call.
+ *   - bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   - Every array is contiguous and row-major.
+ *   - Calls only enqueue work on the given stream and return; they never
+ *     synchronise and never read device memory on the host. A device-side
+ *     fault surfaces at the caller's next synchronisation.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code. Argument checks run
+ *     before anything is enqueued; on an error nothing is enqueued.
+ *   - Calls on different streams with different workspaces are independent.
+ *     Calls that share a workspace must be ordered by the caller.
+ *
+ * Quantised weight format (Lily-ES "Precarga..."; the Lily-HE prefill section
+ * says the same): every 64 consecutive weights along the input (K) dimension
+ * form a group that shares one bf16 scale s and one bf16 bias b; the weight is
+ * w = s * q + b with the 4-bit code q in 0..15. Codes are packed eight to a
+ * uint32, low nibble first: q[n][8c+i] = (Wq[n][c] >> 4i) & 15.
+ *
+ * Numerics of the GPU path: each 64-weight group is rebuilt in registers as
+ * fp16 values fp16(s*(q-8) + (b+8s)), which is within one fp16 rounding of
+ * s*q + b for scales of at least 2^-14; activations enter the matrix cores as
+ * fp16 (bf16 inputs convert exactly while |x| < 65504) and products accumulate
+ * in fp32. The routed expert intermediate h is held as fp16.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK            0
+#define MOE_EINVAL       -1  /* null pointer, bad size, k > E, misaligned pointer */
+#define MOE_EUNSUPPORTED -2  /* d, f or f_sh not a multiple of 64, E > 1024, T too large */
+#define MOE_EWORKSPACE   -3  /* ws_bytes smaller than the size the call needs */
+#define MOE_EHIP         -4  /* the HIP runtime reported an error at launch */
+
+/* Limits. */
+#define MOE_MAX_EXPERTS   1024
+#define MOE_MAX_TOKENS    (1 << 20)  /* per moe_prefill_chunked call */
+#define MOE_MAX_CALL_TOKENS 16384    /* per moe_route / moe_layer_forward call and per chunk */
+#define MOE_BLOCK_ROWS    32  /* rows per block of the block map (32-row tiles) */
+
+/*
+ * One MoE layer (Lily-EN "Three Workload Shapes": a router scores E experts
+ * and picks k, plus one shared expert that sees every token). The expert FFN
+ * is SwiGLU: a = W_gu x, h = silu(a[0:f]) * a[f:2f], o = W_dn h.
+ *
+ *   gu_q  [E][2f][d/8]   gu_s, gu_b  [E][2f][d/64]  rows 0..f-1 gate, f..2f-1 up
+ *   dn_q  [E][d][f/8]    dn_s, dn_b  [E][d][f/64]
+ *   sh_*  the same for the shared expert without the E dimension and with
+ *         f_sh in place of f; f_sh == 0 means the layer has no shared expert
+ *         and the sh_* pointers are ignored.
+ * All weight pointers must be 16-byte aligned.
+ */
+typedef struct moe_layer {
+  int32_t d, f, E, k, f_sh;
+  const uint32_t *gu_q;    const uint16_t *gu_s,    *gu_b;
+  const uint32_t *dn_q;    const uint16_t *dn_s,    *dn_b;
+  const uint32_t *sh_gu_q; const uint16_t *sh_gu_s, *sh_gu_b;
+  const uint32_t *sh_dn_q; const uint16_t *sh_dn_s, *sh_dn_b;
+} moe_layer_t;
+
+/*
+ * Routing outputs for T tokens (Lily-EN "Prefill: Keep Weights Packed, Keep
+ * Routing on the GPU": histogram, prefix scan, scatter and block map all stay
+ * on the GPU). Caller-owned device buffers:
+ *   topk_ids     int32 [T][k]  picked experts, by (logit desc, expert asc);
+ *                equal logits (IEEE ==, so -0.0 == +0.0) go to the lower index
+ *   topk_w       fp32  [T][k]  softmax over the k picked logits
+ *   counts       int32 [E]     pairs (t, j) routed to each expert
+ *   offsets      int32 [E+1]   exclusive prefix sum of counts; offsets[E] = T*k
+ *   sorted_pair  int32 [T*k]   pair index t*k+j of each expert-sorted row;
+ *                stable: ascending t*k+j inside each expert's segment
+ *   sorted_token int32 [T*k]   token of each sorted row
+ *   pair_pos     int32 [T*k]   sorted row of pair t*k+j (inverse permutation)
+ *   block_map    int32 [max_blocks][3] with max_blocks = ceil(T*k/32) + E:
+ *                (expert, first sorted row, rows in 1..32) for every 32-row
+ *                block of every non-empty expert, expert-major; unused
+ *                entries hold (-1, 0, 0)  (Lily-ES "Precarga...": 32-row tiles)
+ *   num_blocks   int32 [1]     number of used block_map entries
+ * Every field must be non-null.
+ */
+typedef struct moe_routing {
+  int32_t *topk_ids; float *topk_w;
+  int32_t *counts, *offsets;
+  int32_t *sorted_pair, *sorted_token, *pair_pos;
+  int32_t *block_map, *num_blocks;
+} moe_routing_t;
+
+/* Number of block_map rows for T tokens: ceil(T*k/32) + E. */
+int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
+
+/*
+ * Bytes of device workspace moe_layer_forward needs for T tokens of layer L
+ * (routing scratch, the fp16 activation copy and the fp16 expert
+ * intermediates; about 27 MB at T=2048, d=2048, f=512, E=256, k=8).
+ * moe_prefill_chunked needs moe_workspace_bytes(chunk, L). Host-only: reads
+ * the scalar fields of L. Returns 0 when the arguments are invalid.
+ */
+size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L);
+
+/* Bytes of device workspace moe_route needs (per-64-token expert bitmasks). */
+size_t moe_route_workspace_bytes(int32_t T, int32_t E);
+
+/*
+ * Routing only. logits fp32 [T][E] (device). Fills every field of *out (the
+ * struct itself is read on the host; its pointers are device pointers).
+ * Errors: MOE_EINVAL (null, T < 0, k < 1, k > E), MOE_EUNSUPPORTED
+ * (E > 1024, T > MOE_MAX_CALL_TOKENS), MOE_EWORKSPACE. T == 0 enqueues
+ * nothing.
+ */
+int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
+              const moe_routing_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped GEMM over uneven expert groups with on-chip int4 dequantisation
+ * (Lily-ES "Precarga...": weights are rebuilt one tile at a time inside the
+ * grouped GEMM and accumulated in FP32; Lily-EN "Prefill..." names the same
+ * fusion). For every block (e, r0, n) of block_map[0 .. *num_blocks) and every
+ * row p in [r0, r0+n):
+ *     C[p][j] = sum_k A[row(p)][k] * W_e[j][k],   j < N, k < K,
+ * with W_e[j][k] = s*q + b from Wq + e*N*(K/8), Ws/Wb + e*N*(K/64), and
+ * row(p) = a_row[p] when a_row is non-null, else p.
+ *   A         bf16 [*][lda], 16-byte aligned, lda % 8 == 0
+ *   Wq        uint32 [G][N][K/8]; Ws, Wb bf16 [G][N][K/64]; 16-byte aligned
+ *   block_map int32 [max_blocks][3] as produced by moe_route; num_blocks [1]
+ *   C         fp32 [*][ldc]; rows not covered by a block are not written
+ * N and K must be multiples of 64; every block has 1..32 rows (the block
+ * map contract). Each block is one work unit of the kernel.
+ */
+int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
+                          int32_t N, int32_t K,
+                          const uint32_t *Wq, const uint16_t *Ws, const uint16_t *Wb,
+                          const int32_t *block_map, const int32_t *num_blocks, int32_t max_blocks,
+                          float *C, int32_t ldc, hipStream_t stream);
+
+/*
+ * The whole layer for T tokens:
+ *     y[t] = sum_j topk_w[t][j] * FFN_(topk_ids[t][j])(x[t]) + FFN_shared(x[t])
+ * x bf16 [T][d]; logits fp32 [T][E]; y fp32 [T][d], fully overwritten.
+ * routing: optional (may be NULL); when given, it receives the routing
+ * tensors of this call. ws: device workspace of at least
+ * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Enqueues four kernels
+ * (top-k, scan/scatter, gate-up, down+combine) and never synchronises.
+ * T == 0 enqueues nothing.
+ */
+int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                      float *y, const moe_routing_t *routing,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_layer_forward with stage timing, for measurement: records events[0]
+ * before the first kernel and events[1..4] after the top-k, scan/scatter,
+ * gate-up and down+combine kernels, all on `stream`. events: 5 caller-created
+ * hipEvent_t handles (host array). Requires T >= 1; otherwise as
+ * moe_layer_forward.
+ */
+int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float *logits,
+                            int32_t T, float *y, const moe_routing_t *routing,
+                            void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *events);
+
+/*
+ * Bounded-chunk prefill for long prompts (Lily-ES "Precarga...", Lily-HE
+ * prefill section: long prompts run in bounded chunks so temporary
+ * activations do not compete with weights for memory). Runs
+ * moe_layer_forward on consecutive chunks of at most `chunk` tokens, in order,
+ * on one stream, reusing one workspace of moe_workspace_bytes(chunk, L)
+ * bytes. Tokens are independent, so y equals the unchunked result; routing
+ * tensors are per chunk and not returned.
+ */
+int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                        int32_t chunk, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. Never NULL. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_INT4_H */

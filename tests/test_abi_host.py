@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/moe_int4.h declares, sizes its workspaces, and rejects bad
+arguments before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_int4_dequant_amd as moe
+from grouped_int4_dequant_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_int4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route", "moe_grouped_gemm_int4", "moe_layer_forward", "moe_prefill_chunked",
+              "moe_workspace_bytes", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def qwen_layer_struct(d=2048, f=512, E=256, k=8, f_sh=512, ptr=0x1000):
+    return B.MoeLayerT(d, f, E, k, f_sh, *([ptr] * 12))
+
+
+def test_workspace_sizes():
+    L = qwen_layer_struct()
+    lib = moe.load()
+    ws = lib.moe_workspace_bytes(2048, ctypes.byref(L))
+    # x16 + h + h_sh dominate: 2048*2048*2 + 16384*512*2 + 2048*512*2
+    big = 2048 * 2048 * 2 + 16384 * 512 * 2 + 2048 * 512 * 2
+    assert big < ws < big + 2 * 2 ** 20
+    assert ws % 256 == 0
+    assert lib.moe_workspace_bytes(2048, ctypes.byref(L)) == lib.moe_workspace_bytes(2048, ctypes.byref(L))
+    assert lib.moe_workspace_bytes(0, ctypes.byref(L)) > 0
+    assert lib.moe_workspace_bytes(-1, ctypes.byref(L)) == 0
+    bad = qwen_layer_struct(d=2000)
+    assert lib.moe_workspace_bytes(2048, ctypes.byref(bad)) == 0
+    assert lib.moe_max_blocks(2048, 256, 8) == 2048 * 8 // 32 + 256
+    assert lib.moe_max_blocks(161, 6, 1) == 12
+    assert lib.moe_route_workspace_bytes(2048, 256) >= 32 * 256 * 8
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(moe.status_string(code), str) and moe.status_string(code)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("d", 2000, B.MOE_EUNSUPPORTED),
+    ("f", 500, B.MOE_EUNSUPPORTED),
+    ("f_sh", 100, B.MOE_EUNSUPPORTED),
+    ("E", 2048, B.MOE_EUNSUPPORTED),
+    ("k", 300, B.MOE_EINVAL),
+    ("k", 0, B.MOE_EINVAL),
+    ("gu_q", None, B.MOE_EINVAL),
+    ("dn_s", 0x1008, B.MOE_EINVAL),   # misaligned
+])
+def test_layer_forward_rejects_bad_layers(field, value, expect):
+    L = qwen_layer_struct()
+    setattr(L, field, value)
+    lib = moe.load()
+    st = lib.moe_layer_forward(ctypes.byref(L), 0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None)
+    assert st == expect
+
+
+def test_layer_forward_rejects_bad_buffers():
+    L = qwen_layer_struct()
+    lib = moe.load()
+    fwd = lambda *a: lib.moe_layer_forward(ctypes.byref(L), *a)
+    assert fwd(None, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None) == B.MOE_EINVAL
+    assert fwd(0x1000, 0x1000, 16, 0x1004, None, 0x1000, 1 << 30, None) == B.MOE_EINVAL  # y misaligned
+    assert fwd(0x1000, 0x1000, -1, 0x1000, None, 0x1000, 1 << 30, None) == B.MOE_EINVAL
+    assert fwd(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 100, None) == B.MOE_EWORKSPACE
+    assert fwd(0x1000, 0x1000, 0, 0x1000, None, 0x1000, 0, None) == B.MOE_OK  # T == 0: no-op
+    assert fwd(0x1000, 0x1000, 1 << 22, 0x1000, None, 0x1000, 1 << 40, None) == B.MOE_EUNSUPPORTED
+
+
+def test_route_and_gemm_reject_bad_arguments():
+    lib = moe.load()
+    r = B.MoeRoutingT(*([0x1000] * 9))
+    assert lib.moe_route(0x1000, 64, 16, 17, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EINVAL
+    assert lib.moe_route(0x1000, 64, 2048, 8, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EUNSUPPORTED
+    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r), 0x1000, 8, None) == B.MOE_EWORKSPACE
+    r0 = B.MoeRoutingT(*([0x1000] * 8 + [None]))
+    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r0), 0x1000, 1 << 20, None) == B.MOE_EINVAL
+    g = lib.moe_grouped_gemm_int4
+    args = [0x1000, 256, None, 128, 256, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 20, 0x1000, 128, None]
+    bad = list(args); bad[3] = 100
+    assert g(*bad) == B.MOE_EUNSUPPORTED
+    bad = list(args); bad[0] = None
+    assert g(*bad) == B.MOE_EINVAL
+    bad = list(args); bad[1] = 100
+    assert g(*bad) == B.MOE_EINVAL
+    bad = list(args); bad[10] = 0
+    assert g(*bad) == B.MOE_OK  # no blocks: nothing to do

@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Routing tensors must match bit for bit; router weights within 1e-6; layer
+outputs within relative Frobenius error 5e-3 and max abs error 2e-2 * rms of
+the oracle output. Large configurations compare every routing tensor and a
+sample of output rows (tokens are independent, so sampled rows are exact
+oracle rows)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import moe_inputs as S
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 5e-3
+MAX_OVER_RMS = 2e-2
+ROUTE_KEYS = ("topk_ids", "counts", "offsets", "sorted_pair", "sorted_token", "pair_pos",
+              "block_map", "num_blocks")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_int4_dequant_amd as m
+    m.load()
+    return m
+
+
+def upload(p: S.Problem, moe):
+    sh = p.shape
+    layer = moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, p.layer)
+    x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+    lg = torch.from_numpy(p.logits).cuda()
+    return layer, x, lg
+
+
+def check_routing(got, ref, T, k):
+    for key in ROUTE_KEYS:
+        g = got[key].cpu().numpy().reshape(-1)
+        r = np.asarray(ref[key]).reshape(-1)
+        assert np.array_equal(g, r), f"routing tensor {key} differs (T={T}, k={k})"
+    w = got["topk_w"].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(w - ref["topk_w"])) <= 1e-6
+
+
+def check_output(y_gpu, y_ref, what=""):
+    m = O.error_metrics(y_gpu, y_ref)
+    say(f"  {what}: rel_fro={m['rel_fro']:.3e} max/rms={m['max_over_rms']:.3e}")
+    assert m["rel_fro"] <= REL_FRO, (what, m)
+    assert m["max_over_rms"] <= MAX_OVER_RMS, (what, m)
+    return m
+
+
+def run_layer(moe, p, with_routing=True):
+    layer, x, lg = upload(p, moe)
+    routing = moe.alloc_routing(p.T, p.shape.E, p.shape.k) if with_routing else None
+    y = moe.layer_forward(layer, x, lg, routing=routing)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), routing
+
+
+# ------------------------------------------------------------------ routing
+def test_route_config0(moe):
+    p = S.make_problem(0)
+    say("route config 0")
+    got = moe.route(torch.from_numpy(p.logits).cuda(), p.shape.k)
+    torch.cuda.synchronize()
+    check_routing(got, O.route(p.logits, p.shape.k), p.T, p.shape.k)
+
+
+def _adversarial_cases():
+    rng = np.random.default_rng(123)
+    cases = []
+    # exact ties including +-0.0
+    L = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(100, 8))
+    cases.append(("ties", L, 3))
+    # all tokens on the same experts
+    L = rng.standard_normal((130, 16)).astype(np.float32)
+    L[:, :4] += 100.0
+    cases.append(("same_experts", L, 4))
+    # counts 31, 32, 33, 64 on experts 0..3 with k = 1 (others empty)
+    L = np.full((160, 6), -5.0, np.float32)
+    rows = np.repeat(np.arange(4), [31, 32, 33, 64])
+    L[np.arange(160), rows] = 5.0
+    cases.append(("edge_counts", L, 1))
+    # k = E
+    cases.append(("k_eq_E", rng.standard_normal((77, 8)).astype(np.float32), 8))
+    # one token, large E
+    cases.append(("one_token", rng.standard_normal((1, 1024)).astype(np.float32), 8))
+    # ragged T, E = 256
+    cases.append(("ragged", rng.standard_normal((1000, 256)).astype(np.float32), 8))
+    # E not a multiple of 64
+    cases.append(("E_odd", rng.standard_normal((300, 67)).astype(np.float32), 5))
+    return cases
+
+
+@pytest.mark.parametrize("name,L,k", _adversarial_cases(), ids=[c[0] for c in _adversarial_cases()])
+def test_route_adversarial(moe, name, L, k):
+    say(f"route adversarial {name} T={L.shape[0]} E={L.shape[1]} k={k}")
+    got = moe.route(torch.from_numpy(L).cuda(), k)
+    torch.cuda.synchronize()
+    check_routing(got, O.route(L, k), L.shape[0], k)
+
+
+def test_route_deterministic(moe):
+    p = S.make_problem(2)
+    say("route determinism T=2048 x10")
+    lg = torch.from_numpy(p.logits).cuda()
+    first = {k_: v.clone() for k_, v in moe.route(lg, 8).items()}
+    for _ in range(10):
+        again = moe.route(lg, 8)
+        for key in first:
+            assert torch.equal(first[key], again[key]), key
+
+
+# ----------------------------------------------------------- grouped GEMM
+@pytest.mark.parametrize("N,K,E,k,T", [(128, 256, 5, 2, 100), (192, 320, 3, 1, 70), (256, 2048, 4, 2, 40)])
+def test_grouped_gemm_matches_oracle(moe, N, K, E, k, T):
+    say(f"grouped gemm N={N} K={K} E={E} k={k} T={T}")
+    rng = np.random.default_rng(N + K)
+    Wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint32)
+    Ws = S.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 64)).astype(np.float32))
+    Wb = S.f32_to_bf16_bits((-8 * O.bf16_value(Ws) * (1 + rng.uniform(-0.1, 0.1, Ws.shape))).astype(np.float32))
+    A = S.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ref_r = O.route(L, k)
+    r = moe.route(torch.from_numpy(L).cuda(), k)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).cuda()
+    C = torch.full((T * k, N), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm_int4(dev(A, np.int16).view(torch.bfloat16), r["sorted_token"], N, K,
+                          dev(Wq, np.int32), dev(Ws, np.int16).view(torch.bfloat16),
+                          dev(Wb, np.int16).view(torch.bfloat16), r["block_map"], r["num_blocks"], C)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    X = O.bf16_value(A)
+    ref = np.zeros((T * k, N))
+    for e in range(E):
+        lo, hi = ref_r["offsets"][e], ref_r["offsets"][e + 1]
+        W = O.dequant(Wq[e], Ws[e], Wb[e])
+        ref[lo:hi] = X[ref_r["sorted_token"][lo:hi]] @ W.T
+    check_output(Cg, ref, "grouped gemm")
+
+
+# ------------------------------------------------------------------ layer
+def test_layer_config0(moe):
+    p = S.make_problem(0)
+    say("layer config 0 (T=64 d=256 f=128 E=16 k=2)")
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, p.shape.k), "config 0")
+
+
+EDGE_SHAPES = [
+    # T, d, f, E, k, f_sh
+    (1, 256, 128, 16, 2, 128),
+    (65, 64, 64, 3, 1, 0),
+    (129, 320, 192, 8, 8, 64),
+    (200, 128, 64, 1, 1, 0),
+    (33, 2048, 512, 256, 8, 512),
+    (300, 512, 320, 12, 3, 192),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,f_sh", EDGE_SHAPES)
+def test_layer_edge_shapes(moe, T, d, f, E, k, f_sh):
+    say(f"layer edge T={T} d={d} f={f} E={E} k={k} f_sh={f_sh}")
+    p = S.make_custom(T, S.LayerShape(d=d, f=f, E=E, k=k, f_sh=f_sh), seed=T + d + f)
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, k), T, k)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"edge {T},{d},{f},{E},{k},{f_sh}")
+
+
+def test_layer_all_tokens_one_expert_set(moe):
+    """Every token routed to the same k experts: each expert group is a dense GEMM."""
+    shape = S.LayerShape(d=256, f=128, E=16, k=2, f_sh=128)
+    p = S.make_custom(300, shape, seed=5)
+    p.logits[:, 3] += 100.0
+    p.logits[:, 11] += 100.0
+    say("layer all tokens on experts 3 and 11")
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, 2), 300, 2)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, 2), "dense special case")
+
+
+def _sample(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n, replace=False)]))
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_layer_full_config(moe, index):
+    p = S.make_problem(index)
+    say(f"layer config {index} T={p.T} (routing full, outputs sampled)")
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
+    tok = _sample(p.T, seed=index)
+    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+    check_output(y[tok], y_ref, f"config {index} sampled")
+
+
+def test_chunked_config3(moe):
+    p = S.make_problem(3)
+    say("config 3: T=8192 in 2048-token chunks (skewed)")
+    layer, x, lg = upload(p, moe)
+    y = moe.prefill_chunked(layer, x, lg, chunk=2048)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref_chunks = O.route_chunks(p.logits, p.shape.k, 2048)
+    for c, ref in enumerate(ref_chunks):
+        got = moe.route(lg[c * 2048:(c + 1) * 2048].contiguous(), p.shape.k)
+        torch.cuda.synchronize()
+        check_routing(got, ref, 2048, p.shape.k)
+        say(f"  chunk {c}: touched experts {int((ref['counts'] > 0).sum())}, max rows {int(ref['counts'].max())}")
+    tok = _sample(p.T, n=64, seed=3)
+    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+    check_output(y[tok], y_ref, "config 3 sampled")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_config4(moe, T):
+    say(f"config 4 decode T={T}: 60 steps")
+    cache = {}
+    layer = None
+    ys, refs = [], []
+    for step, p in enumerate(S.decode_steps(T, steps=60)):
+        if layer is None:
+            layer, _, _ = upload(p, moe)
+        x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+        lg = torch.from_numpy(p.logits).cuda()
+        routing = moe.alloc_routing(T, p.shape.E, p.shape.k)
+        y = moe.layer_forward(layer, x, lg, routing=routing)
+        torch.cuda.synchronize()
+        check_routing(routing, O.route(p.logits, p.shape.k), T, p.shape.k)
+        if step % 20 == 0 or step == 59:
+            ys.append(y.cpu().numpy())
+            refs.append(O.moe_forward(p.layer, p.x, p.logits, p.shape.k, weight_cache=cache))
+    check_output(np.concatenate(ys), np.concatenate(refs), f"decode T={T}")
+
+
+def test_zero_tokens_is_a_noop(moe):
+    p = S.make_problem(0)
+    layer, x, lg = upload(p, moe)
+    y = torch.full((0, p.shape.d), 1.0, device="cuda")
+    moe.layer_forward(layer, x[:0], lg[:0], y=y)
+    torch.cuda.synchronize()
