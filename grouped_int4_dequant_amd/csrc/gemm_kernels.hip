@@ -9,29 +9,30 @@
 // of 64 weights sharing one bf16 scale and one bf16 bias and the 32-row
 // tiles). That design targeted Metal tensor ops on bf16; on gfx950 it becomes:
 //
-//   * Work unit: up to 128 rows (four 32-row blocks) of one expert x one
+//   * Work unit: up to 96 rows (three 32-row blocks) of one expert x one
 //     N-slice of the weights. A workgroup is 4 waves; a wave owns 64 weight
 //     rows (output columns) as four 16-column MFMA blocks and every row of
-//     the unit, so each rebuilt weight feeds every row of the unit.
-//   * Weights go HBM -> VGPR with 128-bit loads, one step ahead of use, and
-//     are rebuilt in registers: v_and_or_b32 puts two codes into fp16 "1024+q"
-//     slots, v_pk_add_f16 removes 1032 exactly, v_pk_fma_f16 applies the group
-//     scale and bias: w = fp16(s*(q-8) + (b+8s)). Only registers hold the
-//     rebuilt tile; nothing expanded is written anywhere.
+//     the unit, so each rebuilt weight feeds every row of the unit. Two
+//     workgroups share a CU (48 KiB of LDS, at most 256 registers per lane),
+//     so one's memory waits overlap the other's math.
+//   * Weights go HBM -> VGPR with one 128-bit load per lane and column block
+//     per K step, one step ahead of use, and are rebuilt in registers:
+//     v_and_or_b32 puts two codes into fp16 "1024+v" slots, v_pk_add_f16
+//     removes the offset exactly, v_pk_fma_f16 applies the group scale and
+//     bias: w = fp16(s*(q-8) + (b+8s)). Only registers hold the rebuilt tile.
 //   * Activations (fp16, each 8-run stored as 0,4,1,5,2,6,3,7 to match the
 //     register order of the rebuilt codes) are gathered by row with 128-bit
 //     loads one step ahead and written to LDS, double buffered, XOR-swizzled
 //     so the 16 rows read by one MFMA operand fetch hit distinct banks.
-//   * v_mfma_f32_16x16x32_f16, fp32 accumulators in AGPRs. 16-row MFMA blocks
-//     let a partial 32-row block skip its empty half.
+//   * v_mfma_f32_16x16x32_f16 with fp32 accumulators. 16-row MFMA blocks let
+//     a partial 32-row block skip its empty half.
 //   * Epilogues: SwiGLU into fp16 h (gate/up projection); weighted combine
 //     into fp32 y with atomics (down projection); plain fp32 store
 //     (stand-alone grouped GEMM).
 //
-// K loop: the four 16-lane quarters of a wave split K into four contiguous
-// ranges; at step s quarter kq handles group kq*steps + s, so a lane reads 32
-// contiguous bytes of codes and one scale/bias per column per step. K is
-// padded to a multiple of 256 with zero weights.
+// K loop: the four 16-lane quarters of a wave split K (padded to a multiple
+// of 128 with zero weights) into four contiguous ranges; at step s quarter kq
+// handles the 32 inputs starting at kq*Kp/4 + 32s, which lie in one 64-group.
 //
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -49,16 +50,17 @@ namespace {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kThreads / 64;
 constexpr int kCB = 4;                            // 16-column MFMA blocks per wave
-constexpr int kRowBytes = 512;                    // one row of one K step: 4 quarters x 64 fp16
-constexpr int kBufBytes = kUnitRows * kRowBytes;  // one K step of a 128-row unit (64 KiB)
-
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+constexpr int kKStep = 128;                       // K per step (4 quarters x 32)
+constexpr int kRowBytes = kKStep * 2;             // one row of one step in LDS (fp16)
+constexpr int kBufBytes = kUnitRows * kRowBytes;  // one step of a full unit (24 KiB)
+constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 
 struct BStage {
-  u4 q[kCB][2];        // 8 code words (64 codes) per column block
+  u4 q[kCB];           // 4 code words (32 codes) per column block
   uint32_t s[kCB];     // bf16 scale bits
   uint32_t b[kCB];     // bf16 bias bits
 };
@@ -99,11 +101,13 @@ struct Unit {
 template <int MODE, bool AF16, int RB32>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, const int *s_tok, const float *s_gw) {
-  constexpr int kMaxRB = 2 * RB32;                          // 16-row MFMA blocks
-  constexpr int kInstA = (32 * RB32 / 2 + kWaves - 1) / kWaves;  // A slabs per wave
+  constexpr int kMaxRB = 2 * RB32;                                       // 16-row MFMA blocks
+  constexpr int kSlabs = (32 * RB32 / kSlabRows + kWaves - 1) / kWaves;  // A stores per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
-  const int N = P.N, K = P.K, G = K >> 6, steps = (K + 255) >> 8;
+  const int N = P.N, K = P.K, G = K >> 6;
+  const int kp4 = ((K + kKStep - 1) / kKStep) * (kKStep / 4);  // K range of one quarter
+  const int steps = kp4 / 32;
   const int nr = U.nr, nrb = (nr + 15) >> 4;
 
   // columns (weight rows) of this wave
@@ -131,31 +135,33 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint16_t *wbi = P.Wb + (int64_t)U.e * P.ws_estride;
   const int kw = K >> 3;
 
+  // first input of this lane's quarter at step s (valid iff < K)
+  auto lane_k0 = [&](int s) { return kq * kp4 + 32 * s; };
+
   auto load_b = [&](BStage &st, int s) {
-    const int g = kq * steps + s;
-    const int gc = g < G ? g : 0;
+    const int k0 = lane_k0(s);
+    const int kc = k0 < K ? k0 : 0;
+    const int g = kc >> 6;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
-      const u4 *p = reinterpret_cast<const u4 *>(wq + (int64_t)ncol[cb] * kw + 8 * gc);
-      st.q[cb][0] = p[0];
-      st.q[cb][1] = p[1];
-      st.s[cb] = wsc[(int64_t)ncol[cb] * G + gc];
-      st.b[cb] = wbi[(int64_t)ncol[cb] * G + gc];
+      st.q[cb] = *reinterpret_cast<const u4 *>(wq + (int64_t)ncol[cb] * kw + (kc >> 3));
+      st.s[cb] = wsc[(int64_t)ncol[cb] * G + g];
+      st.b[cb] = wbi[(int64_t)ncol[cb] * G + g];
     }
   };
 
   // A tile of step s -> LDS buffer, staged through registers. Slot (row r,
   // 16-byte position p) of a buffer holds logical chunk p ^ (r & 15):
-  // quarter (chunk >> 3), 8-run (chunk & 7). One 1 KiB slab = rows 2i, 2i+1.
-  uint4 a_regs[kInstA];
+  // quarter (chunk >> 2), 8-run (chunk & 3). A 1 KiB wave store = 4 rows.
+  uint4 a_regs[kSlabs];
   auto load_a = [&](int s) {
 #pragma unroll
-    for (int ii = 0; ii < kInstA; ++ii) {
+    for (int ii = 0; ii < kSlabs; ++ii) {
       const int i = wave + kWaves * ii;
-      const int r = 2 * i + (lane >> 5);
-      const int ch = (lane & 31) ^ (r & 15);
-      const int g = (ch >> 3) * steps + s;
-      const int kel = g < G ? 64 * g + 8 * (ch & 7) : 0;
+      const int r = kSlabRows * i + (lane >> 4);
+      const int ch = (lane & 15) ^ (r & 15);
+      const int kc = (ch >> 2) * kp4 + 32 * s;
+      const int kel = kc < K ? kc + 8 * (ch & 3) : 0;
       const int64_t row = s_arow[min(r, nr - 1)];
       a_regs[ii] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.A) +
                                                     row * P.lda + kel);
@@ -164,7 +170,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   auto store_a = [&](int buf) {
     uint8_t *dst0 = lds + buf * kBufBytes;
 #pragma unroll
-    for (int ii = 0; ii < kInstA; ++ii) {
+    for (int ii = 0; ii < kSlabs; ++ii) {
       const int i = wave + kWaves * ii;
       uint4 o = a_regs[ii];
       if (!AF16) {  // natural-order bf16 run -> permuted fp16 run
@@ -194,12 +200,12 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
 
   auto compute = [&](const BStage &st, int s, int buf) {
-    const bool gvalid = kq * steps + s < G;
+    const bool kvalid = lane_k0(s) < K;
     h2 s1[kCB], s16[kCB], cc[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       float sf = bf16_bits_to_float(st.s[cb]), bf = bf16_bits_to_float(st.b[cb]);
-      if (!gvalid) sf = bf = 0.f;
+      if (!kvalid) sf = bf = 0.f;
       const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f), ch = (_Float16)(bf + 8.f * sf);
       s1[cb] = h2{sh, sh};
       s16[cb] = h2{sh16, sh16};
@@ -209,11 +215,11 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     const h2 off16 = h2{(_Float16)-1152.f, (_Float16)-1152.f};
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       h8 bfrag[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const uint32_t w = j < 4 ? st.q[cb][0][j] : st.q[cb][1][j - 4];
+        const uint32_t w = st.q[cb][j];
         const uint32_t w8 = w >> 8;
         // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
         const h2 t0 = __builtin_bit_cast(h2, (w & m_lo) | magic) + off1;
@@ -226,7 +232,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
         const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
         bfrag[cb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
       }
-      const int aoff = 16 * ((8 * kq + j) ^ c16);
+      const int aoff = 16 * ((4 * kq + j) ^ c16);
 #pragma unroll
       for (int rb = 0; rb < kMaxRB; ++rb) {
         if (rb < nrb) {
@@ -320,7 +326,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 }
 
 template <int MODE, bool AF16>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
   __shared__ int s_arow[kUnitRows];
   __shared__ int s_tok[kUnitRows];
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs args) {
     const int32_t *u = P.units + 3 * (int64_t)unit;
     U.e = u[0];
     U.r0 = u[1];
-    U.nr = u[2];
+    U.nr = min(u[2], kUnitRows);
   } else {
     U.e = 0;
     U.r0 = unit * kUnitRows;
@@ -363,8 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs args) {
   switch ((U.nr + 31) >> 5) {
     case 1: run_unit<MODE, AF16, 1>(P, U, lds, s_arow, s_tok, s_gw); break;
     case 2: run_unit<MODE, AF16, 2>(P, U, lds, s_arow, s_tok, s_gw); break;
-    case 3: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, s_tok, s_gw); break;
-    default: run_unit<MODE, AF16, 4>(P, U, lds, s_arow, s_tok, s_gw); break;
+    default: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, s_tok, s_gw); break;
   }
 }
 

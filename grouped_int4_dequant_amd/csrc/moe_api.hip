@@ -64,7 +64,6 @@ int check_routing(const moe_routing_t *r) {
 }
 
 struct Workspace {
-  uint64_t *masks;
   moe_routing_t rt;
   int32_t *units, *num_units;
   uint16_t *x16, *h, *h_sh;
@@ -74,10 +73,8 @@ struct Workspace {
 size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   Carver c{base};
   const int E = L->E, k = L->k;
-  const int64_t C = ceil_div(T, kSubChunk);
   const int64_t tk = (int64_t)T * k;
   Workspace o;
-  o.masks = c.take<uint64_t>(C * E);
   o.rt.topk_ids = c.take<int32_t>(tk);
   o.rt.topk_w = c.take<float>(tk);
   o.rt.counts = c.take<int32_t>(E);
@@ -101,7 +98,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
-                  uint64_t *masks, int32_t *units, int32_t *num_units, const uint16_t *x,
+                  int32_t *units, int32_t *num_units, const uint16_t *x,
                   uint16_t *x16, float *y, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
   TopkArgs ta{};
   ta.logits = logits;
@@ -110,15 +107,11 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   ta.k = k;
   ta.topk_ids = rt.topk_ids;
   ta.topk_w = rt.topk_w;
-  ta.masks = masks;
-  ta.n_route_blocks = (int)ceil_div(T, kSubChunk);
   ta.x = x;
   ta.x16 = x16;
   ta.y = y;
   ta.d = d;
-  int n_aux = 0;
-  if (x16) n_aux = (int)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div((int64_t)T * d / 8, 4 * kThreads)));
-  hipError_t err = launch_topk(ta, n_aux, s);
+  hipError_t err = launch_topk(ta, s);
   if (err != hipSuccess) return MOE_EHIP;
   if (record(ev, 1, s) != MOE_OK) return MOE_EHIP;
 
@@ -127,7 +120,6 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   sa.E = E;
   sa.k = k;
   sa.topk_ids = rt.topk_ids;
-  sa.masks = masks;
   sa.counts = rt.counts;
   sa.offsets = rt.offsets;
   sa.sorted_pair = rt.sorted_pair;
@@ -164,7 +156,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
 
   int st = record(ev, 0, s);
   if (st != MOE_OK) return st;
-  st = enqueue_route(logits, T, E, k, rt, w.masks, w.units, w.num_units, x, w.x16, y, d, s, ev);
+  st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, x, w.x16, y, d, s, ev);
   if (st != MOE_OK) return st;
 
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
@@ -247,7 +239,7 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k) {
 
 size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
   if (T < 0 || E <= 0 || E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return 0;
-  return (size_t)round_up(ceil_div(T, kSubChunk) * E * (int64_t)sizeof(uint64_t), kAlign) + kAlign;
+  return kAlign;  // routing keeps its scratch in LDS; the argument is reserved
 }
 
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {
@@ -263,11 +255,11 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_ro
   if (E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
   if (check_routing(out) != MOE_OK) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  if (!logits || !ws) return MOE_EINVAL;
-  if (ws_bytes < moe_route_workspace_bytes(T, E)) return MOE_EWORKSPACE;
-  char *base = reinterpret_cast<char *>(round_up((int64_t)(uintptr_t)ws, kAlign));
-  return enqueue_route(logits, T, E, k, *out, reinterpret_cast<uint64_t *>(base), nullptr, nullptr,
-                       nullptr, nullptr, nullptr, 0, stream);
+  if (!logits) return MOE_EINVAL;
+  (void)ws;
+  (void)ws_bytes;
+  return enqueue_route(logits, T, E, k, *out, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                       stream);
 }
 
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, int32_t N,

@@ -11,7 +11,7 @@
 namespace moe {
 
 constexpr int kGroup = 64;         // weights per scale/bias group
-constexpr int kUnitRows = 128;     // rows of one GEMM work unit (four 32-row blocks)
+constexpr int kUnitRows = 96;      // max rows of one GEMM work unit (three 32-row blocks)
 constexpr int kSubChunk = 64;      // tokens per routing bitmask (one wave's lanes)
 constexpr int kThreads = 256;      // threads per workgroup of every kernel
 
@@ -24,9 +24,7 @@ struct TopkArgs {
   int T, E, k;
   int32_t *topk_ids;
   float *topk_w;
-  uint64_t *masks;          // [ceil(T/64)][E] token bitmask per sub-chunk and expert
-  int n_route_blocks;       // workgroups with the routing role; the rest are auxiliary
-  // auxiliary role (layer forward only; x16 == nullptr disables it)
+  // auxiliary work (layer forward only; x16 == nullptr disables it)
   const uint16_t *x;        // bf16 [T][d]
   uint16_t *x16;            // fp16 [T][d], each 8-element run stored as 0,4,1,5,2,6,3,7
   float *y;                 // fp32 [T][d] zero-filled for the combine
@@ -36,7 +34,6 @@ struct TopkArgs {
 struct ScanArgs {
   int T, E, k;
   const int32_t *topk_ids;
-  const uint64_t *masks;
   int32_t *counts, *offsets, *sorted_pair, *sorted_token, *pair_pos;
   int32_t *block_map, *num_blocks;
   int max_blocks;
@@ -44,7 +41,7 @@ struct ScanArgs {
   int max_units;
 };
 
-hipError_t launch_topk(const TopkArgs &a, int n_aux_blocks, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
 
 // --------------------------------------------------------------- grouped GEMM

@@ -7,16 +7,21 @@
 // la GPU"). Here that is two kernels on one stream whose grids depend only on
 // T, never on routed counts:
 //
-//   topk  one wave per token: the k best logits by (value desc, index asc),
-//         softmax gates over them, and a 64-bit LDS bitmask per expert for
-//         every 64-token sub-chunk (atomicOr is order independent, so the
-//         masks are deterministic). Extra workgroups convert x to fp16 and
-//         zero y for the combine.
-//   scan  one workgroup per sub-chunk: per-expert totals and the sub-chunk's
-//         prefix from popcounts of the masks, the exclusive scan over experts,
-//         and the stable scatter pos = offset[e] + prefix[c][e] +
-//         popcount(mask[c][e] & lanes below t). Workgroup 0 also writes counts,
-//         offsets, the 32-row block map and the GEMM work list.
+//   topk  one wave per token. Every candidate becomes a 64-bit key
+//         (order-preserving logit bits, then the inverted expert index), so
+//         "larger logit, then lower index" is plain unsigned order and all
+//         keys are distinct. k rounds of a wave max (DPP inside each 16-lane
+//         row, readlane across rows) pick the experts; the gates are the
+//         softmax over the k picked logits. The same workgroups then convert
+//         x to fp16 for the GEMMs and zero y for the combine.
+//   scan  one workgroup per 64-token sub-chunk c. Each rebuilds, in LDS, the
+//         per-expert totals, the counts of tokens before its sub-chunk and a
+//         64-bit token mask per expert for its own sub-chunk, scans the totals
+//         into offsets and scatters its pairs stably:
+//           pos = offset[e] + before[e] + popcount(mask[e] & tokens below t).
+//         Integer atomics commute, so the result is deterministic.
+//         Workgroup 0 also writes counts, offsets, the 32-row block map and
+//         the GEMM work list.
 //
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -28,110 +33,118 @@
 
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxVpl = MOE_MAX_EXPERTS / kWave;  // logits per lane at E = 1024
 
-// Strict total order of router candidates: larger logit first; equal logits
-// (IEEE ==, so -0.0 ties +0.0) go to the lower expert index.
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// Order-preserving key: larger logit first, equal logits (IEEE ==, so -0.0
+// ties +0.0) go to the lower expert index. 0 is below every real key.
+__device__ __forceinline__ uint64_t make_key(float v, int e) {
+  uint32_t u = (v == 0.f) ? 0u : __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t two_bf16) {
-  float lo = __uint_as_float(two_bf16 << 16);
-  float hi = __uint_as_float(two_bf16 & 0xFFFF0000u);
-  __half hl = __float2half_rn(lo), hh = __float2half_rn(hi);
-  return (uint32_t)__half_as_ushort(hl) | ((uint32_t)__half_as_ushort(hh) << 16);
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// x (bf16, natural order) -> x16 (fp16, each 8-run stored as 0,4,1,5,2,6,3,7),
-// and y = 0. Grid-stride over the auxiliary workgroups.
-__device__ void aux_role(const TopkArgs &a, int aux_id, int n_aux) {
-  const int64_t n8 = (int64_t)a.T * a.d / 8;
-  const int64_t stride = (int64_t)n_aux * kThreads;
-  for (int64_t i = (int64_t)aux_id * kThreads + threadIdx.x; i < n8; i += stride) {
-    uint4 v = reinterpret_cast<const uint4 *>(a.x)[i];
-    // v.x = (e0,e1) v.y = (e2,e3) v.z = (e4,e5) v.w = (e6,e7)
-    uint32_t p0 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));  // (e0,e4)
-    uint32_t p1 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));  // (e1,e5)
-    uint32_t p2 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));  // (e2,e6)
-    uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));  // (e3,e7)
-    reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
-  }
-  const int64_t n4 = (int64_t)a.T * a.d / 4;
-  for (int64_t i = (int64_t)aux_id * kThreads + threadIdx.x; i < n4; i += stride)
-    reinterpret_cast<float4 *>(a.y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+// Maximum over the 64 lanes, returned uniformly.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+  v = max64(v, dpp64<0xB1>(v));   // quad_perm 1,0,3,2
+  v = max64(v, dpp64<0x4E>(v));   // quad_perm 2,3,0,1
+  v = max64(v, dpp64<0x124>(v));  // row_ror 4
+  v = max64(v, dpp64<0x128>(v));  // row_ror 8: every lane holds its row's maximum
+  return max64(max64(readlane64(v, 0), readlane64(v, 16)),
+               max64(readlane64(v, 32), readlane64(v, 48)));
 }
 
 template <int VPL>
-__device__ void route_role(const TopkArgs &a, int c) {
-  __shared__ unsigned long long smask[MOE_MAX_EXPERTS];
+__device__ void route_token(const TopkArgs &a, int t, int lane) {
   const int E = a.E, k = a.k;
-  for (int e = threadIdx.x; e < E; e += kThreads) smask[e] = 0ull;
-  __syncthreads();
-
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  for (int i = 0; i < kSubChunk / (kThreads / kWave); ++i) {
-    const int tl = wave * (kSubChunk / (kThreads / kWave)) + i;  // token within sub-chunk
-    const int t = c * kSubChunk + tl;
-    if (t >= a.T) break;
-    float v[VPL];
-    const float *row = a.logits + (int64_t)t * E;
+  const float *row = a.logits + (int64_t)t * E;
+  uint64_t key[VPL];
 #pragma unroll
-    for (int r = 0; r < VPL; ++r) {
-      const int e = lane + kWave * r;
-      v[r] = e < E ? row[e] : -__builtin_inff();
-    }
-    uint32_t taken = 0;
-    float sel_v = 0.f;
-    int sel_i = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -__builtin_inff();
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int r = 0; r < VPL; ++r) {
-        const int e = lane + kWave * r;
-        if (e < E && !((taken >> r) & 1u) && better(v[r], e, bv, bi)) { bv = v[r]; bi = e; }
-      }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, kWave);
-        const int oi = __shfl_xor(bi, off, kWave);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi % kWave) == lane) taken |= 1u << (bi / kWave);
-      if (lane == j) { sel_v = bv; sel_i = bi; }
-    }
-    // softmax over the k picked logits (slot 0 holds the largest)
-    const float v0 = __shfl(sel_v, 0, kWave);
-    float ex = lane < k ? expf(sel_v - v0) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
-    if (lane < k) {
-      a.topk_ids[(int64_t)t * k + lane] = sel_i;
-      a.topk_w[(int64_t)t * k + lane] = ex / sum;
-      atomicOr(&smask[sel_i], 1ull << tl);
-    }
+  for (int r = 0; r < VPL; ++r) {
+    const int e = lane + kWave * r;
+    key[r] = e < E ? make_key(row[e], e) : 0ull;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) a.masks[(int64_t)c * E + e] = smask[e];
+  uint32_t taken = 0;
+  float v0 = 0.f, sum = 0.f, my_ex = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0ull;
+    int br = 0;
+#pragma unroll
+    for (int r = 0; r < VPL; ++r)
+      if (!((taken >> r) & 1u) && key[r] > best) { best = key[r]; br = r; }
+    const uint64_t win = wave_max64(best);
+    if (best == win) taken |= 1u << br;  // keys are distinct: one lane wins
+    const float wv = key_value(win);
+    if (j == 0) v0 = wv;
+    const float ex = expf(wv - v0);
+    sum += ex;  // every lane accumulates the same sum, slot order
+    if (lane == j) { my_ex = ex; my_id = key_index(win); }
+  }
+  if (lane < k) {
+    a.topk_ids[(int64_t)t * k + lane] = my_id;
+    a.topk_w[(int64_t)t * k + lane] = my_ex / sum;
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t two_bf16) {
+  const float lo = __uint_as_float(two_bf16 << 16);
+  const float hi = __uint_as_float(two_bf16 & 0xFFFF0000u);
+  return (uint32_t)__half_as_ushort(__float2half_rn(lo)) |
+         ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
 }
 
 template <int VPL>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-  if ((int)blockIdx.x < a.n_route_blocks) {
-    route_role<VPL>(a, blockIdx.x);
-  } else {
-    aux_role(a, blockIdx.x - a.n_route_blocks, gridDim.x - a.n_route_blocks);
+  const int lane = threadIdx.x % kWave;
+  const int gwave = blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int nwaves = gridDim.x * kWaves;
+  for (int t = gwave; t < a.T; t += nwaves) route_token<VPL>(a, t, lane);
+  if (a.x16 == nullptr) return;
+
+  // x (bf16, natural order) -> x16 (fp16, each 8-run stored as 0,4,1,5,2,6,3,7)
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t n8 = (int64_t)a.T * a.d / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = reinterpret_cast<const uint4 *>(a.x)[i];
+    // v.x = (e0,e1) v.y = (e2,e3) v.z = (e4,e5) v.w = (e6,e7)
+    const uint32_t p0 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));  // (e0,e4)
+    const uint32_t p1 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));  // (e1,e5)
+    const uint32_t p2 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));  // (e2,e6)
+    const uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));  // (e3,e7)
+    reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
   }
+  const int64_t n4 = (int64_t)a.T * a.d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<float4 *>(a.y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // Exclusive scan of vals[0..n) (n <= 1024) in LDS by one 256-thread workgroup.
-// Returns the total. scratch must hold kThreads / 64 ints.
+// Returns the total. scratch holds kWaves ints.
 __device__ int block_exclusive_scan(int *vals, int n, int *scratch) {
   const int per = (n + kThreads - 1) / kThreads;  // <= 4
   const int lo = threadIdx.x * per;
@@ -141,7 +154,6 @@ __device__ int block_exclusive_scan(int *vals, int n, int *scratch) {
     local[i] = (lo + i < n) ? vals[lo + i] : 0;
     run += local[i];
   }
-  // inclusive wave scan of run
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   int incl = run;
   for (int off = 1; off < kWave; off <<= 1) {
@@ -151,7 +163,7 @@ __device__ int block_exclusive_scan(int *vals, int n, int *scratch) {
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
   int wave_base = 0, total = 0;
-  for (int w = 0; w < kThreads / kWave; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     if (w < wave) wave_base += scratch[w];
     total += scratch[w];
   }
@@ -168,39 +180,43 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS];
-  __shared__ int s_blk[MOE_MAX_EXPERTS];
-  __shared__ int s_unit[MOE_MAX_EXPERTS];
-  __shared__ int s_scratch[kThreads / kWave];
+  __shared__ int s_aux[MOE_MAX_EXPERTS];
+  __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
+  __shared__ int s_scratch[kWaves];
   const int E = a.E, k = a.k, T = a.T;
   const int c = blockIdx.x;
-  const int C = (T + kSubChunk - 1) / kSubChunk;
+  const int64_t tk = (int64_t)T * k;
+  const int64_t lo = (int64_t)c * kSubChunk * k;
+  const int64_t hi = min(tk, lo + (int64_t)kSubChunk * k);
 
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    int tot = 0, pre = 0;
-    for (int cc = 0; cc < C; ++cc) {
-      const int pc = __popcll(a.masks[(int64_t)cc * E + e]);
-      if (cc < c) pre += pc;
-      tot += pc;
-    }
-    s_tot[e] = tot;
-    s_pre[e] = pre;
-    s_off[e] = tot;
+    s_tot[e] = 0;
+    s_pre[e] = 0;
+    s_mask[e] = 0ull;
   }
+  __syncthreads();
+  for (int64_t idx = threadIdx.x; idx < tk; idx += kThreads) {
+    const int e = a.topk_ids[idx];
+    atomicAdd(&s_tot[e], 1);
+    if (idx < lo) atomicAdd(&s_pre[e], 1);
+    else if (idx < hi) atomicOr(&s_mask[e], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) s_off[e] = s_tot[e];
   __syncthreads();
   const int total = block_exclusive_scan(s_off, E, s_scratch);  // == T*k
 
   // stable scatter of this sub-chunk's (token, slot) pairs
-  for (int idx = threadIdx.x; idx < kSubChunk * k; idx += kThreads) {
-    const int tl = idx / k, j = idx % k;
-    const int t = c * kSubChunk + tl;
-    if (t >= T) continue;
-    const int e = a.topk_ids[(int64_t)t * k + j];
-    const uint64_t m = a.masks[(int64_t)c * E + e];
+  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads) {
+    const int t = (int)(idx / k);
+    const int tl = t - c * kSubChunk;
+    const int e = a.topk_ids[idx];
+    const uint64_t m = s_mask[e];
     const uint64_t below = tl == 0 ? 0ull : (m & ((1ull << tl) - 1ull));
     const int pos = s_off[e] + s_pre[e] + __popcll(below);
-    a.sorted_pair[pos] = t * k + j;
+    a.sorted_pair[pos] = (int)idx;
     a.sorted_token[pos] = t;
-    a.pair_pos[(int64_t)t * k + j] = pos;
+    a.pair_pos[idx] = pos;
   }
   if (c != 0) return;
 
@@ -208,16 +224,15 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   for (int e = threadIdx.x; e < E; e += kThreads) {
     a.counts[e] = s_tot[e];
     a.offsets[e] = s_off[e];
-    s_blk[e] = (s_tot[e] + MOE_BLOCK_ROWS - 1) / MOE_BLOCK_ROWS;
-    s_unit[e] = (s_tot[e] + kUnitRows - 1) / kUnitRows;
+    s_aux[e] = (s_tot[e] + MOE_BLOCK_ROWS - 1) / MOE_BLOCK_ROWS;
   }
   if (threadIdx.x == 0) a.offsets[E] = total;
   __syncthreads();
-  const int nblocks = block_exclusive_scan(s_blk, E, s_scratch);
+  const int nblocks = block_exclusive_scan(s_aux, E, s_scratch);
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const int tot = s_tot[e];
     for (int b = 0; b * MOE_BLOCK_ROWS < tot; ++b) {
-      int32_t *ent = a.block_map + 3 * (int64_t)(s_blk[e] + b);
+      int32_t *ent = a.block_map + 3 * (int64_t)(s_aux[e] + b);
       ent[0] = e;
       ent[1] = s_off[e] + b * MOE_BLOCK_ROWS;
       ent[2] = min(MOE_BLOCK_ROWS, tot - b * MOE_BLOCK_ROWS);
@@ -231,14 +246,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   if (threadIdx.x == 0) *a.num_blocks = nblocks;
   if (a.units == nullptr) return;
   __syncthreads();
-  const int nunits = block_exclusive_scan(s_unit, E, s_scratch);
+  // work list: each expert's rows split evenly into ceil(rows / kUnitRows) units
+  for (int e = threadIdx.x; e < E; e += kThreads) s_aux[e] = (s_tot[e] + kUnitRows - 1) / kUnitRows;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) s_pre[e] = s_aux[e];  // units per expert
+  const int nunits = block_exclusive_scan(s_aux, E, s_scratch);
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e];
-    for (int u = 0; u * kUnitRows < tot; ++u) {
-      int32_t *ent = a.units + 3 * (int64_t)(s_unit[e] + u);
+    const int tot = s_tot[e], nu = s_pre[e];
+    for (int u = 0; u < nu; ++u) {
+      const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
+      int32_t *ent = a.units + 3 * (int64_t)(s_aux[e] + u);
       ent[0] = e;
-      ent[1] = s_off[e] + u * kUnitRows;
-      ent[2] = min(kUnitRows, tot - u * kUnitRows);
+      ent[1] = s_off[e] + b0;
+      ent[2] = b1 - b0;
     }
   }
   if (threadIdx.x == 0) *a.num_units = nunits;
@@ -246,9 +266,12 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs &a, int n_aux_blocks, hipStream_t s) {
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   const int vpl = (a.E + kWave - 1) / kWave;
-  const dim3 grid(a.n_route_blocks + n_aux_blocks), block(kThreads);
+  int nwg = (int)ceil_div(a.T, kWaves);
+  if (a.x16) nwg = (int)std::max<int64_t>(nwg, std::min<int64_t>(1024, ceil_div((int64_t)a.T * a.d / 8, 4 * kThreads)));
+  nwg = std::min(nwg, 4096);
+  const dim3 grid(nwg), block(kThreads);
   if (vpl <= 1)       hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, a);
   else if (vpl <= 2)  hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
   else if (vpl <= 4)  hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
@@ -258,7 +281,7 @@ hipError_t launch_topk(const TopkArgs &a, int n_aux_blocks, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
-  const int C = (a.T + kSubChunk - 1) / kSubChunk;
+  const int C = (int)ceil_div(a.T, kSubChunk);
   hipLaunchKernelGGL(scan_kernel, dim3(C), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -128,15 +128,16 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
  */
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L);
 
-/* Bytes of device workspace moe_route needs (per-64-token expert bitmasks). */
+/* Bytes of device workspace moe_route accepts (routing keeps its scratch in
+ * LDS; the workspace arguments of moe_route are reserved and may be null). */
 size_t moe_route_workspace_bytes(int32_t T, int32_t E);
 
 /*
  * Routing only. logits fp32 [T][E] (device). Fills every field of *out (the
  * struct itself is read on the host; its pointers are device pointers).
  * Errors: MOE_EINVAL (null, T < 0, k < 1, k > E), MOE_EUNSUPPORTED
- * (E > 1024, T > MOE_MAX_CALL_TOKENS), MOE_EWORKSPACE. T == 0 enqueues
- * nothing.
+ * (E > 1024, T > MOE_MAX_CALL_TOKENS). T == 0 enqueues nothing. Launches
+ * two kernels (top-k, then histogram/scan/scatter/block map).
  */
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
               const moe_routing_t *out, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -51,7 +51,8 @@ def test_workspace_sizes():
     assert lib.moe_workspace_bytes(2048, ctypes.byref(bad)) == 0
     assert lib.moe_max_blocks(2048, 256, 8) == 2048 * 8 // 32 + 256
     assert lib.moe_max_blocks(161, 6, 1) == 12
-    assert lib.moe_route_workspace_bytes(2048, 256) >= 32 * 256 * 8
+    assert lib.moe_route_workspace_bytes(2048, 256) > 0
+    assert lib.moe_route_workspace_bytes(2048, 4096) == 0
 
 
 def test_status_strings():
@@ -94,7 +95,8 @@ def test_route_and_gemm_reject_bad_arguments():
     r = B.MoeRoutingT(*([0x1000] * 9))
     assert lib.moe_route(0x1000, 64, 16, 17, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EINVAL
     assert lib.moe_route(0x1000, 64, 2048, 8, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EUNSUPPORTED
-    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r), 0x1000, 8, None) == B.MOE_EWORKSPACE
+    assert lib.moe_route(0x1000, 0, 16, 2, ctypes.byref(r), None, 0, None) == B.MOE_OK  # T == 0
+    assert lib.moe_route(None, 64, 16, 2, ctypes.byref(r), None, 0, None) == B.MOE_EINVAL
     r0 = B.MoeRoutingT(*([0x1000] * 8 + [None]))
     assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r0), 0x1000, 1 << 20, None) == B.MOE_EINVAL
     g = lib.moe_grouped_gemm_int4
