@@ -10,11 +10,13 @@
 // tiles). That design targeted Metal tensor ops on bf16; on gfx950 it becomes:
 //
 //   * Work unit: up to 96 rows (three 32-row blocks) of one expert x one
-//     N-slice of the weights. A workgroup is 4 waves; a wave owns 64 weight
-//     rows (output columns) as four 16-column MFMA blocks and every row of
-//     the unit, so each rebuilt weight feeds every row of the unit. Two
-//     workgroups share a CU (48 KiB of LDS, at most 256 registers per lane),
-//     so one's memory waits overlap the other's math.
+//     512-column N-slice of the weights. A workgroup is 8 waves (two per
+//     SIMD, at most 256 registers per lane); a wave owns 64 weight rows
+//     (output columns) as four 16-column MFMA blocks and every row of the
+//     unit, so each rebuilt weight feeds every row of the unit, and the
+//     unit's activation rows are staged once for 512 columns.
+//   * Each group's scale and bias are read once per work unit with coalesced
+//     loads into an LDS table of fp16 (s, b + 8s) pairs.
 //   * Weights go HBM -> VGPR with one 128-bit load per lane and column block
 //     per K step, one step ahead of use, and are rebuilt in registers:
 //     v_and_or_b32 puts two codes into fp16 "1024+v" slots, v_pk_add_f16
@@ -26,13 +28,15 @@
 //     so the 16 rows read by one MFMA operand fetch hit distinct banks.
 //   * v_mfma_f32_16x16x32_f16 with fp32 accumulators. 16-row MFMA blocks let
 //     a partial 32-row block skip its empty half.
-//   * Epilogues: SwiGLU into fp16 h (gate/up projection); weighted combine
-//     into fp32 y with atomics (down projection); plain fp32 store
-//     (stand-alone grouped GEMM).
+//   * Epilogues: SwiGLU into fp16 h (gate/up projection); fp16 expert
+//     outputs (down projection; a separate kernel combines them per token in
+//     a fixed order); plain fp32 store (stand-alone grouped GEMM).
 //
-// K loop: the four 16-lane quarters of a wave split K (padded to a multiple
-// of 128 with zero weights) into four contiguous ranges; at step s quarter kq
-// handles the 32 inputs starting at kq*Kp/4 + 32s, which lie in one 64-group.
+// K loop: step s covers inputs [128s, 128s+128) (K is padded to a multiple of
+// 128 with zero weights); 16-lane quarter kq takes the 32 inputs starting at
+// 128s + 32kq, which lie in one 64-group. The four lanes of one column thus
+// read 64 contiguous bytes of codes per step, and the other half of that
+// 128-byte line on the next step, so each line is fetched from HBM once.
 //
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -52,18 +56,28 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = kGemmThreads / 64;
 constexpr int kCB = 4;                            // 16-column MFMA blocks per wave
 constexpr int kKStep = 128;                       // K per step (4 quarters x 32)
 constexpr int kRowBytes = kKStep * 2;             // one row of one step in LDS (fp16)
 constexpr int kBufBytes = kUnitRows * kRowBytes;  // one step of a full unit (24 KiB)
 constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 
+constexpr int kCols = kWaves * 64;                // weight rows (output columns) per workgroup
+constexpr int kTabGroups = 32;                     // scale/bias groups held at a time (2048 inputs)
+constexpr int kTabStride = kCols + 16;             // dwords per group row of the table (padded)
+
 struct BStage {
   u4 q[kCB];           // 4 code words (32 codes) per column block
-  uint32_t s[kCB];     // bf16 scale bits
-  uint32_t b[kCB];     // bf16 bias bits
 };
+
+__device__ __forceinline__ uint32_t pack_scale_bias(uint32_t s_bits, uint32_t b_bits) {
+  // (fp16 s, fp16 (b + 8 s)): the per-group constants of the rebuilt weight
+  const float sf = __uint_as_float(s_bits << 16), bf = __uint_as_float(b_bits << 16);
+  const uint32_t lo = __half_as_ushort(__float2half_rn(sf));
+  const uint32_t hi = __half_as_ushort(__float2half_rn(bf + 8.f * sf));
+  return lo | (hi << 16);
+}
 
 // A VGPR holding a constant, so v_and_or_b32 can take the mask from a VGPR
 // and the fp16 magic from an SGPR (VOP3 on gfx9 takes no literal).
@@ -71,10 +85,6 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
   uint32_t r;
   asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
   return r;
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) {
-  return __uint_as_float(bits << 16);
 }
 
 // Workgroup barrier that first drains this wave's LDS operations. The memory
@@ -98,29 +108,31 @@ struct Unit {
   int slice;
 };
 
-template <int MODE, bool AF16, int RB32>
+// NRB = 16-row MFMA blocks of the unit (1..6), fixed at compile time so a K
+// step is one branch-free block the compiler can schedule as a whole.
+template <int MODE, bool AF16, int NRB>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
-                                         const int *s_arow, const int *s_tok, const float *s_gw) {
-  constexpr int kMaxRB = 2 * RB32;                                       // 16-row MFMA blocks
-  constexpr int kSlabs = (32 * RB32 / kSlabRows + kWaves - 1) / kWaves;  // A stores per wave
+                                         const int *s_arow, uint32_t *tab) {
+  constexpr int kMaxRB = NRB;
+  constexpr int kRB32 = (NRB + 1) / 2;                                    // 32-row blocks staged
+  constexpr int kSlabs = (32 * kRB32 / kSlabRows + kWaves - 1) / kWaves;  // A stores per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int N = P.N, K = P.K, G = K >> 6;
-  const int kp4 = ((K + kKStep - 1) / kKStep) * (kKStep / 4);  // K range of one quarter
-  const int steps = kp4 / 32;
-  const int nr = U.nr, nrb = (nr + 15) >> 4;
+  const int steps = (K + kKStep - 1) / kKStep;
+  const int nr = U.nr;
 
   // columns (weight rows) of this wave
   int ncol[kCB];
   bool active;
   if (MODE == kSwiGLU) {
-    const int f = N >> 1, ng = U.slice * 128 + wave * 32;
+    const int f = N >> 1, ng = U.slice * 256 + wave * 32;
     active = ng < f;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
       ncol[cb] = (cb < 2 ? ng + 16 * cb : f + ng + 16 * (cb - 2)) + c16;
   } else {
-    const int n0 = U.slice * 256 + wave * 64;
+    const int n0 = U.slice * 512 + wave * 64;
     active = n0 < N;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) ncol[cb] = n0 + 16 * cb + c16;
@@ -130,42 +142,88 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     for (int cb = 0; cb < kCB; ++cb) ncol[cb] = c16;
   }
 
+  // table column of each of this lane's column blocks, and the weight row of
+  // a table column (-1 past the end)
+  int tcol[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+    tcol[cb] = (MODE == kSwiGLU ? (cb < 2 ? 32 * wave + 16 * cb : kCols / 2 + 32 * wave + 16 * (cb - 2))
+                                : 64 * wave + 16 * cb) + c16;
+  auto tab_row = [&](int c) -> int {
+    if (MODE == kSwiGLU) {
+      const int f = N >> 1, n = U.slice * (kCols / 2) + (c & (kCols / 2 - 1));
+      return n < f ? (c < kCols / 2 ? n : f + n) : -1;
+    }
+    const int n = U.slice * kCols + c;
+    return n < N ? n : -1;
+  };
+
   const uint32_t *wq = P.Wq + (int64_t)U.e * P.wq_estride;
   const uint16_t *wsc = P.Ws + (int64_t)U.e * P.ws_estride;
   const uint16_t *wbi = P.Wb + (int64_t)U.e * P.ws_estride;
   const int kw = K >> 3;
 
   // first input of this lane's quarter at step s (valid iff < K)
-  auto lane_k0 = [&](int s) { return kq * kp4 + 32 * s; };
+  auto lane_k0 = [&](int s) { return kKStep * s + 32 * kq; };
 
   auto load_b = [&](BStage &st, int s) {
     const int k0 = lane_k0(s);
     const int kc = k0 < K ? k0 : 0;
-    const int g = kc >> 6;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb)
       st.q[cb] = *reinterpret_cast<const u4 *>(wq + (int64_t)ncol[cb] * kw + (kc >> 3));
-      st.s[cb] = wsc[(int64_t)ncol[cb] * G + g];
-      st.b[cb] = wbi[(int64_t)ncol[cb] * G + g];
+  };
+
+  // Scale/bias table for groups [32 gc, 32 gc + 32): tab[g][c] holds
+  // (fp16 s, fp16 (b + 8 s)) of group g of table column c. Filled with
+  // coalesced loads once per 2048 inputs instead of per step and lane.
+  auto fill_table = [&](int gc) {
+    const int g0 = kTabGroups * gc, GC = min(kTabGroups, G - g0);
+    if ((G & 7) == 0 && (GC & 7) == 0) {
+      const int per = GC >> 3;  // 8-group vectors per column
+      for (int i = tid; i < kCols * per; i += kGemmThreads) {
+        const int c = i / per, q8 = i - c * per;
+        const int n = tab_row(c);
+        uint4 sv = make_uint4(0, 0, 0, 0), bv = sv;
+        if (n >= 0) {
+          sv = *reinterpret_cast<const uint4 *>(wsc + (int64_t)n * G + g0 + 8 * q8);
+          bv = *reinterpret_cast<const uint4 *>(wbi + (int64_t)n * G + g0 + 8 * q8);
+        }
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          tab[(8 * q8 + 2 * u) * kTabStride + c] = n >= 0 ? pack_scale_bias(sw[u] & 0xFFFFu, bw[u] & 0xFFFFu) : 0u;
+          tab[(8 * q8 + 2 * u + 1) * kTabStride + c] = n >= 0 ? pack_scale_bias(sw[u] >> 16, bw[u] >> 16) : 0u;
+        }
+      }
+    } else {
+      for (int i = tid; i < kCols * GC; i += kGemmThreads) {
+        const int c = i / GC, gg = i - c * GC;
+        const int n = tab_row(c);
+        tab[gg * kTabStride + c] =
+            n >= 0 ? pack_scale_bias(wsc[(int64_t)n * G + g0 + gg], wbi[(int64_t)n * G + g0 + gg]) : 0u;
+      }
     }
   };
 
   // A tile of step s -> LDS buffer, staged through registers. Slot (row r,
   // 16-byte position p) of a buffer holds logical chunk p ^ (r & 15):
-  // quarter (chunk >> 2), 8-run (chunk & 3). A 1 KiB wave store = 4 rows.
+  // quarter (chunk >> 2), 8-run (chunk & 3). One 1 KiB wave store covers 4
+  // rows. bf16 activations are converted to fp16 on the way.
+  auto a_src = [&](int s, int i) {
+    const int r = kSlabRows * i + (lane >> 4);
+    const int ch = (lane & 15) ^ (r & 15);
+    const int kc = kKStep * s + 32 * (ch >> 2);
+    const int kel = kc < K ? kc + 8 * (ch & 3) : 0;
+    const int64_t row = s_arow[min(r, nr - 1)];
+    return reinterpret_cast<const uint16_t *>(P.A) + row * P.lda + kel;
+  };
+
   uint4 a_regs[kSlabs];
   auto load_a = [&](int s) {
 #pragma unroll
-    for (int ii = 0; ii < kSlabs; ++ii) {
-      const int i = wave + kWaves * ii;
-      const int r = kSlabRows * i + (lane >> 4);
-      const int ch = (lane & 15) ^ (r & 15);
-      const int kc = (ch >> 2) * kp4 + 32 * s;
-      const int kel = kc < K ? kc + 8 * (ch & 3) : 0;
-      const int64_t row = s_arow[min(r, nr - 1)];
-      a_regs[ii] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(P.A) +
-                                                    row * P.lda + kel);
-    }
+    for (int ii = 0; ii < kSlabs; ++ii)
+      a_regs[ii] = *reinterpret_cast<const uint4 *>(a_src(s, wave + kWaves * ii));
   };
   auto store_a = [&](int buf) {
     uint8_t *dst0 = lds + buf * kBufBytes;
@@ -200,22 +258,24 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
 
   auto compute = [&](const BStage &st, int s, int buf) {
-    const bool kvalid = lane_k0(s) < K;
+    const int k0 = lane_k0(s);
+    const bool kvalid = k0 < K;
+    const int gt = ((k0 >> 6) & (kTabGroups - 1)) * kTabStride;  // group row in the table
     h2 s1[kCB], s16[kCB], cc[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
-      float sf = bf16_bits_to_float(st.s[cb]), bf = bf16_bits_to_float(st.b[cb]);
-      if (!kvalid) sf = bf = 0.f;
-      const _Float16 sh = (_Float16)sf, sh16 = (_Float16)(sf * 0.0625f), ch = (_Float16)(bf + 8.f * sf);
-      s1[cb] = h2{sh, sh};
-      s16[cb] = h2{sh16, sh16};
-      cc[cb] = h2{ch, ch};
+      const uint32_t tv = kvalid ? tab[gt + tcol[cb]] : 0u;
+      const h2 sc = __builtin_bit_cast(h2, tv);
+      s1[cb] = h2{sc[0], sc[0]};
+      s16[cb] = s1[cb] * h2{(_Float16)0.0625f, (_Float16)0.0625f};
+      cc[cb] = h2{sc[1], sc[1]};
     }
     const h2 off1 = h2{(_Float16)-1032.f, (_Float16)-1032.f};
     const h2 off16 = h2{(_Float16)-1152.f, (_Float16)-1152.f};
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int aoff = 16 * ((4 * kq + j) ^ c16);
       h8 bfrag[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
@@ -232,16 +292,15 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
         const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
         bfrag[cb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
       }
-      const int aoff = 16 * ((4 * kq + j) ^ c16);
+      h8 afr[kMaxRB];
 #pragma unroll
-      for (int rb = 0; rb < kMaxRB; ++rb) {
-        if (rb < nrb) {
-          const h8 a = *reinterpret_cast<const h8 *>(abuf + rb * 16 * kRowBytes + aoff);
+      for (int rb = 0; rb < kMaxRB; ++rb)
+        afr[rb] = *reinterpret_cast<const h8 *>(abuf + rb * 16 * kRowBytes + aoff);
 #pragma unroll
-          for (int cb = 0; cb < kCB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bfrag[cb], acc[rb][cb], 0, 0, 0);
-        }
-      }
+      for (int rb = 0; rb < kMaxRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[rb], bfrag[cb], acc[rb][cb], 0, 0, 0);
     }
   };
 
@@ -252,6 +311,10 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // same number in flight and the compiler's wait counts stay exact.
   auto body = [&](int s, const BStage &cur, BStage &nxt) {
     lds_barrier();
+    if (s > 0 && s < steps && (s & 15) == 0) {  // next 2048 inputs: next table chunk
+      fill_table(s >> 4);
+      lds_barrier();
+    }
     const int sn = min(s + 1, steps - 1);
     load_a(sn);
     load_b(nxt, sn);
@@ -260,6 +323,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   };
 
   BStage b0, b1;
+  fill_table(0);
   load_a(0);
   load_b(b0, 0);
   store_a(0);
@@ -273,10 +337,9 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // accumulator element i of lane (c16, kq) in block (rb, cb) is row
   // 16*rb + 4*kq + i, column 16*cb + c16 of the wave's tile
   if (MODE == kSwiGLU) {
-    const int ng = U.slice * 128 + wave * 32;
+    const int ng = U.slice * 256 + wave * 32;
 #pragma unroll
     for (int rb = 0; rb < kMaxRB; ++rb) {
-      if (rb >= nrb) break;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int col = perm_col(ng + 16 * cb + c16);
@@ -291,34 +354,23 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
         }
       }
     }
-  } else if (MODE == kCombine) {
-    const int n0 = U.slice * 256 + wave * 64;
-#pragma unroll
-    for (int rb = 0; rb < kMaxRB; ++rb) {
-      if (rb >= nrb) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + 4 * kq + i;
-        if (r < nr) {
-          float *yrow = P.Y + (int64_t)s_tok[r] * P.ldy + n0 + c16;
-          const float w = s_gw[r];
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) unsafeAtomicAdd(yrow + 16 * cb, w * acc[rb][cb][i]);
-        }
-      }
-    }
   } else {
-    const int n0 = U.slice * 256 + wave * 64;
+    const int n0 = U.slice * 512 + wave * 64;
 #pragma unroll
     for (int rb = 0; rb < kMaxRB; ++rb) {
-      if (rb >= nrb) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * kq + i;
         if (r < nr) {
-          float *crow = P.C + (int64_t)(U.r0 + r) * P.ldc + n0 + c16;
+          if (MODE == kStoreH) {
+            uint16_t *orow = P.H + (int64_t)(U.r0 + r) * P.ldh + n0 + c16;
 #pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) crow[16 * cb] = acc[rb][cb][i];
+            for (int cb = 0; cb < kCB; ++cb) orow[16 * cb] = f32_to_f16_bits(acc[rb][cb][i]);
+          } else {
+            float *crow = P.C + (int64_t)(U.r0 + r) * P.ldc + n0 + c16;
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) crow[16 * cb] = acc[rb][cb][i];
+          }
         }
       }
     }
@@ -326,11 +378,10 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 }
 
 template <int MODE, bool AF16>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
+  __shared__ uint32_t tab[kTabGroups * kTabStride];
   __shared__ int s_arow[kUnitRows];
-  __shared__ int s_tok[kUnitRows];
-  __shared__ float s_gw[kUnitRows];
 
   const int b = blockIdx.x;
   const bool second = args.nprob > 1 && b >= args.prob[1].wg_begin;
@@ -356,32 +407,31 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs args) {
     if (U.nr <= 0) return;
   }
 
-  for (int r = threadIdx.x; r < kUnitRows; r += kThreads) {
+  for (int r = threadIdx.x; r < kUnitRows; r += kGemmThreads) {
     const int p = U.r0 + min(r, U.nr - 1);
     s_arow[r] = P.a_row ? P.a_row[p] : p;
-    if (MODE == kCombine) {
-      s_tok[r] = P.row_token ? P.row_token[p] : p;
-      s_gw[r] = P.pair_w ? P.pair_w[P.row_pair[p]] : 1.f;
-    }
   }
   __syncthreads();
 
-  switch ((U.nr + 31) >> 5) {
-    case 1: run_unit<MODE, AF16, 1>(P, U, lds, s_arow, s_tok, s_gw); break;
-    case 2: run_unit<MODE, AF16, 2>(P, U, lds, s_arow, s_tok, s_gw); break;
-    default: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, s_tok, s_gw); break;
+  switch ((U.nr + 15) >> 4) {
+    case 1: run_unit<MODE, AF16, 1>(P, U, lds, s_arow, tab); break;
+    case 2: run_unit<MODE, AF16, 2>(P, U, lds, s_arow, tab); break;
+    case 3: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, tab); break;
+    case 4: run_unit<MODE, AF16, 4>(P, U, lds, s_arow, tab); break;
+    case 5: run_unit<MODE, AF16, 5>(P, U, lds, s_arow, tab); break;
+    default: run_unit<MODE, AF16, 6>(P, U, lds, s_arow, tab); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s) {
-  const dim3 grid(a.total_wg), block(kThreads);
+  const dim3 grid(a.total_wg), block(kGemmThreads);
   if (a.total_wg == 0) return hipSuccess;
   if (a_f16) {
     switch (mode) {
       case kSwiGLU: hipLaunchKernelGGL((gemm_kernel<kSwiGLU, true>), grid, block, 0, s, a); break;
-      case kCombine: hipLaunchKernelGGL((gemm_kernel<kCombine, true>), grid, block, 0, s, a); break;
+      case kStoreH: hipLaunchKernelGGL((gemm_kernel<kStoreH, true>), grid, block, 0, s, a); break;
       default: hipLaunchKernelGGL((gemm_kernel<kStoreC, true>), grid, block, 0, s, a); break;
     }
   } else {

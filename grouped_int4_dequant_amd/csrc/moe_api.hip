@@ -66,7 +66,7 @@ int check_routing(const moe_routing_t *r) {
 struct Workspace {
   moe_routing_t rt;
   int32_t *units, *num_units;
-  uint16_t *x16, *h, *h_sh;
+  uint16_t *x16, *h, *h_sh, *o, *o_sh;
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
@@ -89,6 +89,8 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
   o.h = c.take<uint16_t>((size_t)tk * L->f);
   o.h_sh = c.take<uint16_t>((size_t)T * L->f_sh);
+  o.o = c.take<uint16_t>((size_t)tk * L->d);
+  o.o_sh = c.take<uint16_t>(L->f_sh > 0 ? (size_t)T * L->d : 0);
   if (w) *w = o;
   return (size_t)round_up((int64_t)c.off, kAlign);
 }
@@ -99,7 +101,7 @@ int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
                   int32_t *units, int32_t *num_units, const uint16_t *x,
-                  uint16_t *x16, float *y, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
+                  uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
   TopkArgs ta{};
   ta.logits = logits;
   ta.T = T;
@@ -109,7 +111,6 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   ta.topk_w = rt.topk_w;
   ta.x = x;
   ta.x16 = x16;
-  ta.y = y;
   ta.d = d;
   hipError_t err = launch_topk(ta, s);
   if (err != hipSuccess) return MOE_EHIP;
@@ -156,7 +157,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
 
   int st = record(ev, 0, s);
   if (st != MOE_OK) return st;
-  st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, x, w.x16, y, d, s, ev);
+  st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, x, w.x16, d, s, ev);
   if (st != MOE_OK) return st;
 
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
@@ -169,7 +170,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = 2 * fs; p.K = d;
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
-    p.nslices = (int)ceil_div(fs, 128);
+    p.nslices = (int)ceil_div(fs, 256);
     p.wg_begin = nwg;
     p.H = w.h_sh; p.ldh = fs;
     nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
@@ -181,7 +182,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)2 * f * (d / 8); p.ws_estride = (int64_t)2 * f * (d / 64);
     p.N = 2 * f; p.K = d;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
-    p.nslices = (int)ceil_div(f, 128);
+    p.nslices = (int)ceil_div(f, 256);
     p.wg_begin = nwg;
     p.H = w.h; p.ldh = f;
     nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
@@ -192,7 +193,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   if (st == MOE_OK) st = record(ev, 3, s);
   if (st != MOE_OK) return st;
 
-  // down projection + weighted combine into y (zeroed by the routing kernel)
+  // down projection into fp16 expert outputs, then the weighted combine
   GemmArgs g2{};
   nwg = 0;
   np = 0;
@@ -203,9 +204,9 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = d; p.K = fs;
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
-    p.nslices = (int)ceil_div(d, 256);
+    p.nslices = (int)ceil_div(d, 512);
     p.wg_begin = nwg;
-    p.Y = y; p.ldy = d; p.row_token = nullptr; p.row_pair = nullptr; p.pair_w = nullptr;
+    p.H = w.o_sh; p.ldh = d;
     nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
   }
   {
@@ -215,15 +216,26 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)d * (f / 8); p.ws_estride = (int64_t)d * (f / 64);
     p.N = d; p.K = f;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
-    p.nslices = (int)ceil_div(d, 256);
+    p.nslices = (int)ceil_div(d, 512);
     p.wg_begin = nwg;
-    p.Y = y; p.ldy = d;
-    p.row_token = rt.sorted_token; p.row_pair = rt.sorted_pair; p.pair_w = rt.topk_w;
+    p.H = w.o; p.ldh = d;
     nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
   }
   g2.nprob = np;
   g2.total_wg = nwg;
-  st = hip_status(launch_gemm(g2, kCombine, true, s));
+  st = hip_status(launch_gemm(g2, kStoreH, true, s));
+  if (st != MOE_OK) return st;
+
+  CombineArgs ca{};
+  ca.T = T;
+  ca.d = d;
+  ca.k = k;
+  ca.o = w.o;
+  ca.o_sh = fs > 0 ? w.o_sh : nullptr;
+  ca.pair_pos = rt.pair_pos;
+  ca.topk_w = rt.topk_w;
+  ca.y = y;
+  st = hip_status(launch_combine(ca, s));
   if (st == MOE_OK) st = record(ev, 4, s);
   return st;
 }
@@ -258,8 +270,7 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_ro
   if (!logits) return MOE_EINVAL;
   (void)ws;
   (void)ws_bytes;
-  return enqueue_route(logits, T, E, k, *out, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-                       stream);
+  return enqueue_route(logits, T, E, k, *out, nullptr, nullptr, nullptr, nullptr, 0, stream);
 }
 
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, int32_t N,
@@ -279,7 +290,7 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, 
   p.wq_estride = (int64_t)N * (K / 8); p.ws_estride = (int64_t)N * (K / 64);
   p.N = N; p.K = K;
   p.units = block_map; p.num_units = num_blocks; p.implicit_rows = 0;
-  p.nslices = (int)ceil_div(N, 256);
+  p.nslices = (int)ceil_div(N, 512);
   p.wg_begin = 0;
   p.C = C; p.ldc = ldc;
   g.nprob = 1;

@@ -13,7 +13,8 @@ namespace moe {
 constexpr int kGroup = 64;         // weights per scale/bias group
 constexpr int kUnitRows = 96;      // max rows of one GEMM work unit (three 32-row blocks)
 constexpr int kSubChunk = 64;      // tokens per routing bitmask (one wave's lanes)
-constexpr int kThreads = 256;      // threads per workgroup of every kernel
+constexpr int kThreads = 256;      // threads per workgroup of the routing and combine kernels
+constexpr int kGemmThreads = 512;  // threads per workgroup of the grouped GEMM (8 waves)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -27,8 +28,17 @@ struct TopkArgs {
   // auxiliary work (layer forward only; x16 == nullptr disables it)
   const uint16_t *x;        // bf16 [T][d]
   uint16_t *x16;            // fp16 [T][d], each 8-element run stored as 0,4,1,5,2,6,3,7
-  float *y;                 // fp32 [T][d] zero-filled for the combine
   int d;
+};
+
+// y[t] = sum_j w[t][j] * o[pair_pos[t*k+j]] + o_sh[t], slot order, fp32.
+struct CombineArgs {
+  int T, d, k;
+  const uint16_t *o;        // fp16 [T*k][d] routed expert outputs, expert-sorted rows
+  const uint16_t *o_sh;     // fp16 [T][d] shared expert outputs (nullptr: none)
+  const int32_t *pair_pos;  // [T*k]
+  const float *topk_w;      // [T][k]
+  float *y;                 // fp32 [T][d]
 };
 
 struct ScanArgs {
@@ -43,13 +53,14 @@ struct ScanArgs {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 // --------------------------------------------------------------- grouped GEMM
 // Epilogue modes of the grouped GEMM kernel.
 enum GemmMode : int {
-  kStoreC = 0,    // C[p][n] = acc                         (stand-alone GEMM)
-  kSwiGLU = 1,    // H[p][n] = fp16(silu(acc_gate) * acc_up) (gate/up projection)
-  kCombine = 2,   // Y[t][n] += w_p * acc  (fp32 atomics)      (down projection)
+  kStoreC = 0,    // C[p][n] = acc (fp32)                     (stand-alone GEMM)
+  kSwiGLU = 1,    // H[p][n] = fp16(silu(acc_gate) * acc_up)  (gate/up projection)
+  kStoreH = 2,    // H[p][n] = fp16(acc)                      (down projection)
 };
 
 // One grouped problem: a list of work units (expert, first row, rows) over a
@@ -68,12 +79,8 @@ struct GemmProblem {
   int nslices;               // workgroups per unit along N
   int wg_begin;              // first workgroup (in remapped order) of this problem
   // outputs
-  float *C; int ldc;                                    // kStoreC
-  uint16_t *H; int ldh;                                 // kSwiGLU
-  float *Y; int ldy;                                    // kCombine
-  const int32_t *row_token;   // kCombine: token of row p (nullptr: p)
-  const int32_t *row_pair;    // kCombine: pair index of row p (gate = pair_w[row_pair[p]])
-  const float *pair_w;        // kCombine: nullptr gives weight 1
+  float *C; int ldc;          // kStoreC
+  uint16_t *H; int ldh;       // kSwiGLU (permuted-run columns), kStoreH (natural columns)
 };
 
 struct GemmArgs {

@@ -13,7 +13,7 @@
 //         keys are distinct. k rounds of a wave max (DPP inside each 16-lane
 //         row, readlane across rows) pick the experts; the gates are the
 //         softmax over the k picked logits. The same workgroups then convert
-//         x to fp16 for the GEMMs and zero y for the combine.
+//         x to fp16 for the GEMMs.
 //   scan  one workgroup per 64-token sub-chunk c. Each rebuilds, in LDS, the
 //         per-expert totals, the counts of tokens before its sub-chunk and a
 //         64-bit token mask per expert for its own sub-chunk, scans the totals
@@ -138,9 +138,39 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     const uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));  // (e3,e7)
     reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
   }
-  const int64_t n4 = (int64_t)a.T * a.d / 4;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride)
-    reinterpret_cast<float4 *>(a.y)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ void add_f16x8(float *acc, uint4 v, float w) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += w * __half2float(__ushort_as_half((uint16_t)(u[i] & 0xFFFFu)));
+    acc[2 * i + 1] += w * __half2float(__ushort_as_half((uint16_t)(u[i] >> 16)));
+  }
+}
+
+// Weighted combine (the fourth part of the layer): one workgroup per token,
+// eight outputs per thread, terms added in slot order then the shared
+// expert, so y is reproducible bit for bit.
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int k = a.k;
+  __shared__ int s_pos[MOE_MAX_EXPERTS];
+  __shared__ float s_w[MOE_MAX_EXPERTS];
+  for (int j = threadIdx.x; j < k; j += kThreads) {
+    s_pos[j] = a.pair_pos[(int64_t)t * k + j];
+    s_w[j] = a.topk_w[(int64_t)t * k + j];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 8; c < a.d; c += kThreads * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j)
+      add_f16x8(acc, *reinterpret_cast<const uint4 *>(a.o + (int64_t)s_pos[j] * a.d + c), s_w[j]);
+    if (a.o_sh) add_f16x8(acc, *reinterpret_cast<const uint4 *>(a.o_sh + (int64_t)t * a.d + c), 1.f);
+    float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * a.d + c);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
 }
 
 // Exclusive scan of vals[0..n) (n <= 1024) in LDS by one 256-thread workgroup.
@@ -195,11 +225,24 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
     s_mask[e] = 0ull;
   }
   __syncthreads();
-  for (int64_t idx = threadIdx.x; idx < tk; idx += kThreads) {
-    const int e = a.topk_ids[idx];
-    atomicAdd(&s_tot[e], 1);
-    if (idx < lo) atomicAdd(&s_pre[e], 1);
-    else if (idx < hi) atomicOr(&s_mask[e], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+  // loads are batched (kBatch independent loads in flight per thread)
+  constexpr int kBatch = 16;
+  for (int64_t base = threadIdx.x; base < tk; base += (int64_t)kThreads * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t idx = base + (int64_t)u * kThreads;
+      ids[u] = idx < tk ? a.topk_ids[idx] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t idx = base + (int64_t)u * kThreads;
+      const int e = ids[u];
+      if (e < 0) continue;
+      atomicAdd(&s_tot[e], 1);
+      if (idx < lo) atomicAdd(&s_pre[e], 1);
+      else if (idx < hi) atomicOr(&s_mask[e], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) s_off[e] = s_tot[e];
@@ -277,6 +320,11 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   else if (vpl <= 4)  hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
   else if (vpl <= 8)  hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
   else                hipLaunchKernelGGL(topk_kernel<kMaxVpl>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

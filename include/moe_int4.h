@@ -43,7 +43,8 @@
  * fp16 values fp16(s*(q-8) + (b+8s)), which is within one fp16 rounding of
  * s*q + b for scales of at least 2^-14; activations enter the matrix cores as
  * fp16 (bf16 inputs convert exactly while |x| < 65504) and products accumulate
- * in fp32. The routed expert intermediate h is held as fp16.
+ * in fp32. The expert intermediates h and the expert outputs are held as
+ * fp16 (so they must stay below 65504 in magnitude); y is fp32.
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H
@@ -121,8 +122,9 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
 
 /*
  * Bytes of device workspace moe_layer_forward needs for T tokens of layer L
- * (routing scratch, the fp16 activation copy and the fp16 expert
- * intermediates; about 27 MB at T=2048, d=2048, f=512, E=256, k=8).
+ * (routing scratch, the fp16 activation copy, the fp16 expert
+ * intermediates and the fp16 expert outputs; about 102 MB at T=2048,
+ * d=2048, f=512, E=256, k=8).
  * moe_prefill_chunked needs moe_workspace_bytes(chunk, L). Host-only: reads
  * the scalar fields of L. Returns 0 when the arguments are invalid.
  */
@@ -156,7 +158,8 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
  *   block_map int32 [max_blocks][3] as produced by moe_route; num_blocks [1]
  *   C         fp32 [*][ldc]; rows not covered by a block are not written
  * N and K must be multiples of 64; every block has 1..32 rows (the block
- * map contract). Each block is one work unit of the kernel.
+ * map contract; longer blocks are cut at 96 rows). Each block is one work
+ * unit of the kernel.
  */
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
                           int32_t N, int32_t K,
@@ -170,8 +173,10 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
  * x bf16 [T][d]; logits fp32 [T][E]; y fp32 [T][d], fully overwritten.
  * routing: optional (may be NULL); when given, it receives the routing
  * tensors of this call. ws: device workspace of at least
- * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Enqueues four kernels
- * (top-k, scan/scatter, gate-up, down+combine) and never synchronises.
+ * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Enqueues five kernels
+ * (top-k, scan/scatter, gate-up, down, combine) and never synchronises.
+ * The combine adds the k weighted expert rows in slot order and then the
+ * shared expert's row, in fp32, so y is reproducible bit for bit.
  * T == 0 enqueues nothing.
  */
 int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
@@ -181,7 +186,7 @@ int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logi
 /*
  * moe_layer_forward with stage timing, for measurement: records events[0]
  * before the first kernel and events[1..4] after the top-k, scan/scatter,
- * gate-up and down+combine kernels, all on `stream`. events: 5 caller-created
+ * gate-up and down(+combine) kernels, all on `stream`. events: 5 caller-created
  * hipEvent_t handles (host array). Requires T >= 1; otherwise as
  * moe_layer_forward.
  */

@@ -168,6 +168,8 @@ EDGE_SHAPES = [
     (200, 128, 64, 1, 1, 0),
     (33, 2048, 512, 256, 8, 512),
     (300, 512, 320, 12, 3, 192),
+    (50, 2560, 192, 4, 2, 64),      # K = 2560: scale/bias table refilled after 2048 inputs
+    (40, 448, 576, 5, 2, 0),        # 7 groups along d: scalar table fill
 ]
 
 
