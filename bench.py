@@ -29,6 +29,27 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E peak
 METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak)"
 
+# Bytes per launch of each GEMM kernel at T=2048, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) over this benchmark, scaled by what the same counters
+# read for a plain 64 MiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0). They
+# describe the kernels built from the sources with this digest; after any change
+# to those sources the figure is stale and reported as null.
+TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
+                   "grouped_int4_dequant_amd/csrc/moe_internal.h",
+                   "grouped_int4_dequant_amd/csrc/moe_api.hip")
+TRAFFIC_DIGEST = "7476d7b702e0a083b1e27a5904f20bb33299aaf57899ba81d9388a0be5acf4e2"
+TRAFFIC_BYTES = {"gate_up": (190745.7 * 2.0 + 18434.0) * 1024,
+                 "down_combine": (85988.7 * 2.0 + 73728.0 + 37137.1 * 2.0 + 16384.1) * 1024}
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -36,7 +57,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--cpu-tokens", type=int, default=48, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=2048, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before the timed region, run a plain device copy of this many MiB three times "
+                         "(a known-size kernel for calibrating hardware byte counters; 0: none)")
     return ap.parse_args()
 
 
@@ -84,6 +108,14 @@ def main():
         if st != 0:
             raise RuntimeError(moe.status_string(st))
 
+    if args.copy_mb > 0:
+        n = args.copy_mb << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         moe.layer_forward(layer, x, lg, y=y, ws=ws)
     step_events = [make_events(5) for _ in range(args.steps)]
@@ -94,7 +126,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    stages = ["topk", "scan", "gate_up", "down"]
+    stages = ["topk", "scan", "gate_up", "down_combine"]
     dur = {s: float(np.mean([evs[i].elapsed_time(evs[i + 1]) for evs in step_events]))
            for i, s in enumerate(stages)}  # ms
     gpu_ms = float(np.mean([evs[0].elapsed_time(evs[4]) for evs in step_events]))
@@ -102,7 +134,7 @@ def main():
 
     flops_tok_gu = 2 * 2 * sh.d * (sh.k * sh.f + sh.f_sh)  # gate/up: 2 flops x 2f x d per row
     flops_tok_dn = 2 * sh.d * (sh.k * sh.f + sh.f_sh)
-    kern_flops = {"gate_up": flops_tok_gu * T, "down": flops_tok_dn * T}
+    kern_flops = {"gate_up": flops_tok_gu * T, "down_combine": flops_tok_dn * T}
     dom = max(kern_flops, key=lambda s: dur[s])
     achieved = kern_flops[dom] / (dur[dom] * 1e-3) / 1e12
     layer_tflops = (flops_tok_gu + flops_tok_dn) * T / (gpu_ms * 1e-3) / 1e12
@@ -125,7 +157,8 @@ def main():
                    "f_sh": sh.f_sh, "weights": "int4 groupwise-affine g=64 bf16 scale+bias",
                    "inputs": "seeded synthetic (config 2 recipe)"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
+                     "traffic": TRAFFIC_BYTES[dom] if sources_digest() == TRAFFIC_DIGEST else None},
         "stages_us": {s: dur[s] * 1e3 for s in stages},
         "layer": {"gpu_us": gpu_ms * 1e3, "useful_tflops": layer_tflops,
                   "mfma_frac": layer_tflops / MFMA_PEAK_TFLOPS,
@@ -193,13 +226,19 @@ def cpu_baseline(p, ntok):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    ntok = min(ntok, p.T)
     tok = np.arange(ntok)
-    t0 = time.perf_counter()
-    O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
-    dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {ntok} of {p.T} tokens of the T={p.T} workload, fp64 numpy oracle "
-                      f"including dequantisation of every expert they touch ({dt:.1f} s)"}
+    passes, t0 = 0, time.perf_counter()
+    while True:  # whole passes until at least 10 s of CPU work
+        O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0:
+            break
+    what = f"all {p.T} tokens" if ntok == p.T else f"first {ntok} of {p.T} tokens"
+    return {"value": ntok * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} of the T={p.T} workload, {passes} pass(es) of the fp64 numpy oracle, "
+                      f"each dequantising every expert the tokens touch ({dt:.1f} s in total)"}
 
 
 if __name__ == "__main__":
