@@ -179,7 +179,12 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
     weights (about 1.8 GB, larger than the last-level cache) so repeated
     experts are not served from cache. Bytes per step are exact: the packed
     codes, scales and biases of the distinct experts touched plus the shared
-    expert."""
+    expert.
+
+    The steps are captured into one HIP graph and replayed, so the GPU time
+    per step is the device's (a decode loop would run captured steps too);
+    the eager rate of back-to-back calls from Python is reported beside it.
+    The replay's last output is checked against the eager one."""
     cfg = S.CONFIGS[4]
     sh = cfg.shape
     steps = list(S.decode_steps(1, steps=nsteps + 20))
@@ -187,32 +192,56 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
               for _ in range(4)]
     xs = [torch.from_numpy(s.x.view(np.int16)).view(torch.bfloat16).to(dev) for s in steps]
     lgs = [torch.from_numpy(s.logits).to(dev) for s in steps]
-    y = torch.empty((1, sh.d), dtype=torch.float32, device=dev)
+    ys = [torch.empty((1, sh.d), dtype=torch.float32, device=dev) for _ in steps]
     ws = moe.alloc_workspace(moe.workspace_bytes(1, layers[0]), dev)
     per_expert = S.bytes_per_expert(sh)
     nbytes = []
     for s in steps:
         touched = len(np.unique(np.argsort(-s.logits[0], kind="stable")[:sh.k]))
         nbytes.append((touched + 1) * per_expert)
+
+    def run(i):
+        moe.layer_forward(layers[i % 4], xs[i], lgs[i], y=ys[i], ws=ws)
+
     for i in range(20):
-        moe.layer_forward(layers[i % 4], xs[i], lgs[i], y=y, ws=ws)
-    evs_all = [make_events(5) for _ in range(nsteps)]
+        run(i)
     torch.cuda.synchronize()
+    # eager: back-to-back calls
+    e0, e1 = make_events(2)
     t0 = time.perf_counter()
-    for i in range(nsteps):
-        L = layers[i % 4]
-        arr = (B._P * 5)(*[e.cuda_event for e in evs_all[i]])
-        st = lib.moe_layer_forward_timed(B.ctypes.byref(L.c), xs[20 + i].data_ptr(), lgs[20 + i].data_ptr(), 1,
-                                         y.data_ptr(), None, ws.data_ptr(), ws.numel(), stream.cuda_stream, arr)
-        assert st == 0
+    e0.record(stream)
+    for i in range(20, 20 + nsteps):
+        run(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / nsteps
-    gpu = float(np.mean([e[0].elapsed_time(e[4]) for e in evs_all])) * 1e-3
-    gemm = float(np.mean([e[2].elapsed_time(e[4]) for e in evs_all])) * 1e-3
+    eager_gpu = e0.elapsed_time(e1) * 1e-3 / nsteps
+    y_eager = ys[19 + nsteps].clone()
+    # graph: the same steps captured once, replayed
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(20, 20 + nsteps):
+                run(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    g0, g1 = make_events(2)
+    g0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gpu = g0.elapsed_time(g1) * 1e-3 / (reps * nsteps)
+    same = bool(torch.equal(ys[19 + nsteps], y_eager))
     b = float(np.mean(nbytes[20:]))
     return {"T": 1, "steps": nsteps, "bytes_per_step": b,
-            "gpu_us_per_step": gpu * 1e6, "wall_us_per_step": wall * 1e6,
-            "gbps_gpu": b / gpu / 1e9, "gbps_gemm_kernels": b / gemm / 1e9,
+            "gpu_us_per_step": gpu * 1e6, "eager_gpu_us_per_step": eager_gpu * 1e6,
+            "wall_us_per_step": wall * 1e6, "graph_replay_matches_eager": same,
+            "gbps_gpu": b / gpu / 1e9, "gbps_eager": b / eager_gpu / 1e9,
             "frac_hbm_gpu": b / gpu / 1e9 / HBM_PEAK_GBPS, "peak_gbps": HBM_PEAK_GBPS}
 
 

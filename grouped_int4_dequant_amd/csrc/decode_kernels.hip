@@ -1,0 +1,342 @@
+// Decode-shape MoE layer (a few tokens per call) for gfx950: two kernels.
+//
+// At batch-1 decode the layer has almost no weight reuse, so the bytes of
+// the touched experts set the time (Lily-EN "Decode: Minimize Bytes Moved
+// Per Token"; Lily-ES "Decodificar: minimizar los bytes movidos por token").
+// The prefill schedule gives each expert two workgroups; here the same
+// arithmetic is spread over every CU and the launch count is cut to two:
+//
+//   gate/up  one workgroup per (distinct routed expert or the shared expert,
+//            16 columns of h), one wave per 512 inputs.
+//            Every workgroup first repeats the top-k for the call's tokens
+//            (a wave max over order-preserving 64-bit keys, as in the routing
+//            kernel) and ranks the distinct experts with a bitmap, so no
+//            routing kernel runs before it. The waves' partial sums meet in
+//            LDS; SwiGLU gives fp32 h per (token, slot).
+//   down     one workgroup per (token, 16 output columns), one wave per slot
+//            (the k routed experts and the shared expert), 512 inputs each. The partial
+//            projections meet in LDS and are combined in slot order with the
+//            gates: y = sum_j g_j o_j + o_shared, fp32, with no atomics.
+//
+// Weights are rebuilt from the 4-bit codes exactly as in the prefill GEMM
+// (rebuild_device.h) and multiplied with v_mfma_f32_16x16x32_f16; the rows
+// beyond the call's tokens are zero.
+//
+// Pages cited (titles as published):
+//   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
+//            for Qwen3.6-35B-A3B on Apple Silicon" (insight.aitobox.com)
+//   Lily-ES  "Perplexity open sources Lily: un motor de inferencia ... para
+//            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
+
+#include "moe_internal.h"
+#include "rebuild_device.h"
+#include "topk_device.h"
+
+namespace moe {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+constexpr int kSpan = 512;          // inputs per wave
+constexpr int kSteps = kSpan / 128;  // 128-input steps per wave
+constexpr int kMaxWaves = 8;         // gate/up waves per workgroup (d <= 4096)
+
+// Top-k of one token by one wave: lane j < k ends with the id and gate of
+// slot j (slots in descending logit order; gates = softmax over the k picks).
+// Each lane first sorts its own keys, so one round is a wave maximum over the
+// lanes' heads, after which the winning lane shifts its list up by one.
+template <int VPL>
+__device__ void topk_wave(const float *row, int E, int k, int lane, int &my_id, float &my_gate) {
+  uint64_t key[VPL];
+#pragma unroll
+  for (int r = 0; r < VPL; ++r) {
+    const int e = lane + 64 * r;
+    key[r] = e < E ? make_key(row[e], e) : 0ull;
+  }
+  // descending insertion sort of the lane's keys (VPL <= 16, unrolled)
+#pragma unroll
+  for (int i = 1; i < VPL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j)
+      if (key[j] > key[j - 1]) {
+        const uint64_t t = key[j];
+        key[j] = key[j - 1];
+        key[j - 1] = t;
+      }
+  float v0 = 0.f, sum = 0.f, my_ex = 0.f;
+  my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    // wave maximum of the heads: first over the logit half of the key, then
+    // over the index half among the lanes that hold that logit
+    const uint32_t hi = (uint32_t)(key[0] >> 32);
+    const uint32_t mhi = wave_max32(hi);
+    const uint32_t lo = hi == mhi ? (uint32_t)key[0] : 0u;
+    const uint64_t win = ((uint64_t)mhi << 32) | wave_max32(lo);
+    if (key[0] == win) {  // keys are distinct: one lane wins and drops its head
+#pragma unroll
+      for (int r = 0; r + 1 < VPL; ++r) key[r] = key[r + 1];
+      key[VPL - 1] = 0ull;
+    }
+    const float wv = key_value(win);
+    if (j == 0) v0 = wv;
+    const float ex = expf(wv - v0);
+    sum += ex;
+    if (lane == j) { my_ex = ex; my_id = key_index(win); }
+  }
+  my_gate = my_ex / sum;
+}
+
+// Position of the r-th set bit of m (r < popcount(m)).
+__device__ __forceinline__ int nth_bit(uint32_t m, int r) {
+  for (int i = 0; i < r; ++i) m &= m - 1;
+  return __ffs(m) - 1;
+}
+
+// (fp16 s, fp16 b + 8 s) of group 2 s + half from the packed bf16 scales and
+// biases of eight consecutive groups.
+__device__ __forceinline__ uint32_t group_consts(const u4v &sw, const u4v &bw, int s, int half) {
+  const uint32_t sh = 16u * (uint32_t)half;
+  return rb_pack_scale_bias((sw[s] >> sh) & 0xFFFFu, (bw[s] >> sh) & 0xFFFFu);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a) {
+  __shared__ int s_ids[kDecodeMaxPairs];
+  __shared__ uint32_t s_bits[MOE_MAX_EXPERTS / 32];
+  __shared__ int s_uexp[kDecodeMaxPairs];
+  __shared__ uint32_t s_umask[kDecodeMaxPairs];
+  __shared__ int s_U;
+  __shared__ float s_red[kMaxWaves][2][256];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
+  const int T = a.T, k = a.k, E = a.E, P = T * k;
+  const int nwords = (E + 31) / 32;
+
+  const int chunks = a.fmax / 16;
+  const int u = blockIdx.x / chunks, hc = blockIdx.x - u * chunks;
+  const bool shared = u == P;
+
+  // ---- routing, repeated by every workgroup of a routed expert
+  if (!shared) {
+  for (int i = tid; i < nwords; i += nthreads) s_bits[i] = 0u;
+  if (tid < kDecodeMaxPairs) s_umask[tid] = 0u;
+  if (wave == 0) {
+    for (int t = 0; t < T; ++t) {
+      int id;
+      float g;
+      topk_wave<VPL>(a.logits + (int64_t)t * E, E, k, lane, id, g);
+      if (lane < k) {
+        s_ids[t * k + lane] = id;
+        if (blockIdx.x == 0) {
+          a.ids[t * k + lane] = id;
+          a.gates[t * k + lane] = g;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < P) atomicOr(&s_bits[s_ids[tid] >> 5], 1u << (s_ids[tid] & 31));
+  __syncthreads();
+  if (tid < P) {
+    // rank of this expert among the distinct ones (ascending expert index)
+    const int e = s_ids[tid], wi = e >> 5;
+    int rank = __popc(s_bits[wi] & ((1u << (e & 31)) - 1u));
+    for (int q = 0; q < wi; ++q) rank += __popc(s_bits[q]);
+    s_uexp[rank] = e;
+    atomicOr(&s_umask[rank], 1u << (tid / k));
+  }
+  if (tid == 0) {
+    int U = 0;
+    for (int q = 0; q < nwords; ++q) U += __popc(s_bits[q]);
+    s_U = U;
+  }
+  __syncthreads();
+  }
+
+  // ---- this workgroup's item: (distinct expert u or the shared expert, 16 h columns)
+  int e = 0, fe;
+  uint32_t mask;
+  if (shared) {
+    if (a.f_sh == 0) return;
+    fe = a.f_sh;
+    mask = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
+  } else {
+    if (u >= s_U) return;
+    e = s_uexp[u];
+    mask = s_umask[u];
+    fe = a.f;
+  }
+  if (16 * hc >= fe) return;
+  const int nrows = __popc(mask);
+
+  const int d = a.d, G = d / 64;
+  const uint32_t *wq = shared ? a.sh_gu_q : a.gu_q + (int64_t)e * a.gu_qs;
+  const uint16_t *wsc = shared ? a.sh_gu_s : a.gu_s + (int64_t)e * a.gu_ss;
+  const uint16_t *wbi = shared ? a.sh_gu_b : a.gu_b + (int64_t)e * a.gu_ss;
+  const int c16 = lane & 15, kq = lane >> 4;
+  const int row[2] = {16 * hc + c16, fe + 16 * hc + c16};  // gate row, up row
+  const int kbase = wave * kSpan, nwaves = nthreads / 64;
+
+  // ---- requests: codes, scales/biases, activations (all before any use)
+  u4v code[2][kSteps], sw[2], bw[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const uint32_t *cr = wq + (int64_t)row[cb] * (d / 8) + (kbase + 32 * kq) / 8;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) code[cb][s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
+    sw[cb] = *reinterpret_cast<const u4v *>(wsc + (int64_t)row[cb] * G + kbase / 64);
+    bw[cb] = *reinterpret_cast<const u4v *>(wbi + (int64_t)row[cb] * G + kbase / 64);
+  }
+  const bool has_row = c16 < nrows;
+  const int tok = has_row ? nth_bit(mask, c16) : 0;
+  const uint16_t *xr = a.x + (int64_t)tok * d + kbase + 32 * kq;
+  u4v xv[kSteps][4];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xv[s][j] = has_row ? *reinterpret_cast<const u4v *>(xr + 128 * s + 8 * j) : u4v{0u, 0u, 0u, 0u};
+
+  // ---- MFMAs over this wave's inputs
+  const RbConsts kc = rb_consts();
+  f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    uint32_t sc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) sc[cb] = group_consts(sw[cb], bw[cb], s, kq >> 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float xf[8];
+      const u4v w = xv[s][j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xf[2 * i] = __uint_as_float(w[i] << 16);
+        xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      const rb_h8 af = rb_perm8(xf);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, rb_rebuild(code[cb][s][j], sc[cb], kc), acc[cb], 0,
+                                                         0, 0);
+    }
+  }
+
+  // ---- partial sums of the waves meet in LDS; SwiGLU; fp32 h per (token, slot)
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][cb][4 * lane + i] = acc[cb][i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * kq + i;  // row of the MFMA tile = r-th token of the mask
+      if (r < nrows) {
+        float g = 0.f, up = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+          g += s_red[w][0][4 * lane + i];
+          up += s_red[w][1][4 * lane + i];
+        }
+        const int t = nth_bit(mask, r);
+        int slot = k;
+        if (!shared)
+          for (int j = 0; j < k; ++j)
+            if (s_ids[t * k + j] == e) slot = j;
+        a.h[((int64_t)t * (k + 1) + slot) * a.fmax + 16 * hc + c16] = g / (1.f + __expf(-g)) * up;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeArgs a) {
+  __shared__ float s_part[kDecodeMaxSlots][16];
+  const int tid = threadIdx.x, lane = tid & 63, j = tid >> 6;  // wave j: slot j (j == k: shared)
+  const int k = a.k, d = a.d, chunks = d / 16;
+  const int t = blockIdx.x / chunks, cc = blockIdx.x - t * chunks;
+  const int c16 = lane & 15, kq = lane >> 4;
+  const bool shared = j == k;
+  const int fe = shared ? a.f_sh : a.f;
+
+  // gates of this token, requested before anything else (used at the end)
+  __shared__ float s_gate[kDecodeMaxSlots];
+  if (tid < k) s_gate[tid] = a.gates[t * k + tid];
+
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  if (fe > 0) {  // fe == kSpan
+    const int e = shared ? 0 : a.ids[t * k + j];
+    const uint32_t *wq = shared ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
+    const uint16_t *wsc = shared ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
+    const uint16_t *wbi = shared ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
+    const int n = 16 * cc + c16;
+    u4v code[kSteps];
+    const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + 4 * kq;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) code[s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
+    const u4v sw = *reinterpret_cast<const u4v *>(wsc + (int64_t)n * (kSpan / 64));
+    const u4v bw = *reinterpret_cast<const u4v *>(wbi + (int64_t)n * (kSpan / 64));
+    // activations: row 0 of the tile is this token's h for slot j
+    const float *hr = a.h + ((int64_t)t * (k + 1) + j) * a.fmax + 32 * kq;
+    rb_h8 hv[kSteps][4];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float hf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (c16 == 0) {
+          const f4 h0 = *reinterpret_cast<const f4 *>(hr + 128 * s + 8 * q);
+          const f4 h1 = *reinterpret_cast<const f4 *>(hr + 128 * s + 8 * q + 4);
+          hf[0] = h0[0]; hf[1] = h0[1]; hf[2] = h0[2]; hf[3] = h0[3];
+          hf[4] = h1[0]; hf[5] = h1[1]; hf[6] = h1[2]; hf[7] = h1[3];
+        }
+        hv[s][q] = rb_perm8(hf);
+      }
+    const RbConsts kc = rb_consts();
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const uint32_t sc = group_consts(sw, bw, s, kq >> 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hv[s][q], rb_rebuild(code[s][q], sc, kc), acc, 0, 0, 0);
+    }
+  }
+  // row 0, column c16 of the tile sits in lane (c16, kq = 0), element 0
+  if (kq == 0) s_part[j][c16] = acc[0];
+  __syncthreads();
+  if (tid < 16) {
+    float y = 0.f;
+    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * s_part[jj][tid];
+    y += s_part[k][tid];
+    a.y[(int64_t)t * d + 16 * cc + tid] = y;
+  }
+}
+
+}  // namespace
+
+bool decode_supported(int T, const moe_layer_t *L) {
+  return T >= 1 && T <= kDecodeMaxT && T * L->k <= kDecodeMaxPairs && L->k + 1 <= kDecodeMaxSlots &&
+         L->d % kSpan == 0 && L->d / kSpan <= kMaxWaves && L->f == kSpan && (L->f_sh == 0 || L->f_sh == kSpan) &&
+         L->E <= MOE_MAX_EXPERTS;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_mid) {
+  const int vpl = (a.E + 63) / 64;
+  const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
+  if (vpl <= 1)       hipLaunchKernelGGL(decode_gu_kernel<1>, g1, b1, 0, s, a);
+  else if (vpl <= 2)  hipLaunchKernelGGL(decode_gu_kernel<2>, g1, b1, 0, s, a);
+  else if (vpl <= 4)  hipLaunchKernelGGL(decode_gu_kernel<4>, g1, b1, 0, s, a);
+  else if (vpl <= 8)  hipLaunchKernelGGL(decode_gu_kernel<8>, g1, b1, 0, s, a);
+  else                hipLaunchKernelGGL(decode_gu_kernel<16>, g1, b1, 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ev_mid) {
+    err = hipEventRecord(ev_mid, s);
+    if (err != hipSuccess) return err;
+  }
+  const dim3 g2(a.T * (a.d / 16)), b2(64 * (a.k + 1));
+  hipLaunchKernelGGL(decode_dn_kernel, g2, b2, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -180,20 +180,35 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   auto fill_table = [&](int gc) {
     const int g0 = kTabGroups * gc, GC = min(kTabGroups, G - g0);
     if ((G & 7) == 0 && (GC & 7) == 0) {
+      // every load is issued before the first conversion, so the fill costs
+      // one memory round trip
+      constexpr int kIt = kCols * (kTabGroups / 8) / kGemmThreads;
       const int per = GC >> 3;  // 8-group vectors per column
-      for (int i = tid; i < kCols * per; i += kGemmThreads) {
-        const int c = i / per, q8 = i - c * per;
-        const int n = tab_row(c);
-        uint4 sv = make_uint4(0, 0, 0, 0), bv = sv;
-        if (n >= 0) {
-          sv = *reinterpret_cast<const uint4 *>(wsc + (int64_t)n * G + g0 + 8 * q8);
-          bv = *reinterpret_cast<const uint4 *>(wbi + (int64_t)n * G + g0 + 8 * q8);
-        }
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint4 sv[kIt], bv[kIt];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          tab[(8 * q8 + 2 * u) * kTabStride + c] = n >= 0 ? pack_scale_bias(sw[u] & 0xFFFFu, bw[u] & 0xFFFFu) : 0u;
-          tab[(8 * q8 + 2 * u + 1) * kTabStride + c] = n >= 0 ? pack_scale_bias(sw[u] >> 16, bw[u] >> 16) : 0u;
+      for (int it = 0; it < kIt; ++it) {
+        const int i = tid + it * kGemmThreads;
+        const int c = i / per, q8 = i - c * per;
+        const int n = i < kCols * per ? tab_row(c) : -1;
+        sv[it] = bv[it] = make_uint4(0, 0, 0, 0);
+        if (n >= 0) {
+          sv[it] = *reinterpret_cast<const uint4 *>(wsc + (int64_t)n * G + g0 + 8 * q8);
+          bv[it] = *reinterpret_cast<const uint4 *>(wbi + (int64_t)n * G + g0 + 8 * q8);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int i = tid + it * kGemmThreads;
+        if (i < kCols * per) {
+          const int c = i / per, q8 = i - c * per;
+          const bool live = tab_row(c) >= 0;
+          const uint32_t sw[4] = {sv[it].x, sv[it].y, sv[it].z, sv[it].w};
+          const uint32_t bw[4] = {bv[it].x, bv[it].y, bv[it].z, bv[it].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            tab[(8 * q8 + 2 * u) * kTabStride + c] = live ? pack_scale_bias(sw[u] & 0xFFFFu, bw[u] & 0xFFFFu) : 0u;
+            tab[(8 * q8 + 2 * u + 1) * kTabStride + c] = live ? pack_scale_bias(sw[u] >> 16, bw[u] >> 16) : 0u;
+          }
         }
       }
     } else {
@@ -210,20 +225,29 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // 16-byte position p) of a buffer holds logical chunk p ^ (r & 15):
   // quarter (chunk >> 2), 8-run (chunk & 3). One 1 KiB wave store covers 4
   // rows. bf16 activations are converted to fp16 on the way.
-  auto a_src = [&](int s, int i) {
-    const int r = kSlabRows * i + (lane >> 4);
+  // Per slab of this wave: the activation row and the 16-byte chunk this lane
+  // moves, fixed for the whole unit; only the K offset changes per step.
+  const uint16_t *a_row_ptr[kSlabs];
+  int a_q32[kSlabs], a_in[kSlabs];
+#pragma unroll
+  for (int ii = 0; ii < kSlabs; ++ii) {
+    const int r = kSlabRows * (wave + kWaves * ii) + (lane >> 4);
     const int ch = (lane & 15) ^ (r & 15);
-    const int kc = kKStep * s + 32 * (ch >> 2);
-    const int kel = kc < K ? kc + 8 * (ch & 3) : 0;
-    const int64_t row = s_arow[min(r, nr - 1)];
-    return reinterpret_cast<const uint16_t *>(P.A) + row * P.lda + kel;
+    a_row_ptr[ii] = reinterpret_cast<const uint16_t *>(P.A) + (int64_t)s_arow[min(r, nr - 1)] * P.lda;
+    a_q32[ii] = 32 * (ch >> 2);
+    a_in[ii] = 32 * (ch >> 2) + 8 * (ch & 3);
+  }
+  auto a_src = [&](int s, int ii) {
+    const int off = kKStep * s;
+    const int kel = off + a_q32[ii] < K ? off + a_in[ii] : 0;
+    return a_row_ptr[ii] + kel;
   };
 
   uint4 a_regs[kSlabs];
   auto load_a = [&](int s) {
 #pragma unroll
     for (int ii = 0; ii < kSlabs; ++ii)
-      a_regs[ii] = *reinterpret_cast<const uint4 *>(a_src(s, wave + kWaves * ii));
+      a_regs[ii] = *reinterpret_cast<const uint4 *>(a_src(s, ii));
   };
   auto store_a = [&](int buf) {
     uint8_t *dst0 = lds + buf * kBufBytes;
@@ -273,34 +297,49 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     const h2 off1 = h2{(_Float16)-1032.f, (_Float16)-1032.f};
     const h2 off16 = h2{(_Float16)-1152.f, (_Float16)-1152.f};
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
+    // rebuild the 32 codes of quarter-step j for column block cb
+    auto rebuild = [&](int j, int cb) -> h8 {
+      const uint32_t w = st.q[cb][j];
+      const uint32_t w8 = w >> 8;
+      // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
+      const h2 t0 = __builtin_bit_cast(h2, (w & m_lo) | magic) + off1;
+      const h2 t1 = __builtin_bit_cast(h2, (w & m_hi) | magic) + off16;
+      const h2 t2 = __builtin_bit_cast(h2, (w8 & m_lo) | magic) + off1;
+      const h2 t3 = __builtin_bit_cast(h2, (w8 & m_hi) | magic) + off16;
+      const h2 w0 = __builtin_elementwise_fma(t0, s1[cb], cc[cb]);
+      const h2 w1 = __builtin_elementwise_fma(t1, s16[cb], cc[cb]);
+      const h2 w2 = __builtin_elementwise_fma(t2, s1[cb], cc[cb]);
+      const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
+      return h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+    };
+    auto read_a = [&](int j, int rb) -> h8 {
+      const int aoff = 16 * ((4 * kq + j) ^ c16);
+      return *reinterpret_cast<const h8 *>(abuf + rb * 16 * kRowBytes + aoff);
+    };
+    // Software pipeline over the four quarter-steps, one chunk per column
+    // block: the MFMAs of (quarter j, block cb) run while the VALU rebuilds
+    // (quarter j, block cb+1) or (j+1, 0); each rebuilt fragment is written
+    // into registers its block has just finished with. The activation
+    // fragments of quarter j+1 are read from LDS behind the last block's
+    // MFMAs of quarter j. Scheduling barriers keep the chunks in this order.
+    h8 bq[kCB], af[kMaxRB];
+    bq[0] = rebuild(0, 0);
+#pragma unroll
+    for (int rb = 0; rb < kMaxRB; ++rb) af[rb] = read_a(0, rb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int aoff = 16 * ((4 * kq + j) ^ c16);
-      h8 bfrag[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const uint32_t w = st.q[cb][j];
-        const uint32_t w8 = w >> 8;
-        // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
-        const h2 t0 = __builtin_bit_cast(h2, (w & m_lo) | magic) + off1;
-        const h2 t1 = __builtin_bit_cast(h2, (w & m_hi) | magic) + off16;
-        const h2 t2 = __builtin_bit_cast(h2, (w8 & m_lo) | magic) + off1;
-        const h2 t3 = __builtin_bit_cast(h2, (w8 & m_hi) | magic) + off16;
-        const h2 w0 = __builtin_elementwise_fma(t0, s1[cb], cc[cb]);
-        const h2 w1 = __builtin_elementwise_fma(t1, s16[cb], cc[cb]);
-        const h2 w2 = __builtin_elementwise_fma(t2, s1[cb], cc[cb]);
-        const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
-        bfrag[cb] = h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+        if (j == 0 && cb + 1 < kCB) bq[cb + 1] = rebuild(0, cb + 1);
+        if (j + 1 < 4 && cb > 0) bq[cb - 1] = rebuild(j + 1, cb - 1);
+#pragma unroll
+        for (int rb = 0; rb < kMaxRB; ++rb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb], bq[cb], acc[rb][cb], 0, 0, 0);
+          if (cb == kCB - 1 && j + 1 < 4) af[rb] = read_a(j + 1, rb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      h8 afr[kMaxRB];
-#pragma unroll
-      for (int rb = 0; rb < kMaxRB; ++rb)
-        afr[rb] = *reinterpret_cast<const h8 *>(abuf + rb * 16 * kRowBytes + aoff);
-#pragma unroll
-      for (int rb = 0; rb < kMaxRB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[rb], bfrag[cb], acc[rb][cb], 0, 0, 0);
+      if (j + 1 < 4) bq[kCB - 1] = rebuild(j + 1, kCB - 1);
     }
   };
 

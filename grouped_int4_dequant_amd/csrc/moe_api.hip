@@ -67,6 +67,7 @@ struct Workspace {
   moe_routing_t rt;
   int32_t *units, *num_units;
   uint16_t *x16, *h, *h_sh, *o, *o_sh;
+  float *dec_h;  // decode-shape calls only
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
@@ -87,10 +88,15 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E));
   o.num_units = c.take<int32_t>(1);
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
-  o.h = c.take<uint16_t>((size_t)tk * L->f);
-  o.h_sh = c.take<uint16_t>((size_t)T * L->f_sh);
-  o.o = c.take<uint16_t>((size_t)tk * L->d);
-  o.o_sh = c.take<uint16_t>(L->f_sh > 0 ? (size_t)T * L->d : 0);
+  // The shared expert's rows follow the routed rows in h and o when their
+  // widths match, so one grouped GEMM can cover both.
+  const bool joint_h = L->f_sh == L->f;
+  o.h = c.take<uint16_t>((size_t)tk * L->f + (joint_h ? (size_t)T * L->f_sh : 0));
+  o.h_sh = joint_h ? (base ? o.h + (size_t)tk * L->f : nullptr) : c.take<uint16_t>((size_t)T * L->f_sh);
+  o.o = c.take<uint16_t>((size_t)(tk + (L->f_sh > 0 ? T : 0)) * L->d);
+  o.o_sh = (L->f_sh > 0 && base) ? o.o + (size_t)tk * L->d : nullptr;
+  const int fmax = L->f > L->f_sh ? L->f : L->f_sh;
+  o.dec_h = T <= kDecodeMaxT ? c.take<float>((size_t)T * (L->k + 1) * fmax) : nullptr;
   if (w) *w = o;
   return (size_t)round_up((int64_t)c.off, kAlign);
 }
@@ -145,6 +151,22 @@ int record(hipEvent_t *ev, int i, hipStream_t s) {
   return ev ? hip_status(hipEventRecord(ev[i], s)) : MOE_OK;
 }
 
+int enqueue_combine(int T, int d, int k, const uint16_t *o, const uint16_t *o_sh, const moe_routing_t &rt,
+                    float *y, hipStream_t s, hipEvent_t *ev) {
+  CombineArgs ca{};
+  ca.T = T;
+  ca.d = d;
+  ca.k = k;
+  ca.o = o;
+  ca.o_sh = o_sh;
+  ca.pair_pos = rt.pair_pos;
+  ca.topk_w = rt.topk_w;
+  ca.y = y;
+  int st = hip_status(launch_combine(ca, s));
+  if (st == MOE_OK) st = record(ev, 4, s);
+  return st;
+}
+
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
                 hipEvent_t *ev = nullptr) {
@@ -157,6 +179,33 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
 
   int st = record(ev, 0, s);
   if (st != MOE_OK) return st;
+
+  if (decode_supported(T, L)) {
+    // A few tokens: gate/up (routing repeated inside) and down + combine.
+    // Routing tensors are produced by the routing kernels only when asked for.
+    if (routing) {
+      st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, nullptr, nullptr, d, s, ev);
+    } else {
+      st = record(ev, 1, s);
+      if (st == MOE_OK) st = record(ev, 2, s);
+    }
+    if (st != MOE_OK) return st;
+    DecodeArgs a{};
+    a.logits = logits; a.x = x;
+    a.T = T; a.d = d; a.f = f; a.f_sh = fs; a.E = E; a.k = k; a.fmax = f > fs ? f : fs;
+    a.gu_q = L->gu_q; a.gu_s = L->gu_s; a.gu_b = L->gu_b;
+    a.gu_qs = (int64_t)2 * f * (d / 8); a.gu_ss = (int64_t)2 * f * (d / 64);
+    a.dn_q = L->dn_q; a.dn_s = L->dn_s; a.dn_b = L->dn_b;
+    a.dn_qs = (int64_t)d * (f / 8); a.dn_ss = (int64_t)d * (f / 64);
+    a.sh_gu_q = L->sh_gu_q; a.sh_gu_s = L->sh_gu_s; a.sh_gu_b = L->sh_gu_b;
+    a.sh_dn_q = L->sh_dn_q; a.sh_dn_s = L->sh_dn_s; a.sh_dn_b = L->sh_dn_b;
+    a.ids = w.rt.topk_ids; a.gates = w.rt.topk_w;  // the workspace's own routing buffers
+    a.h = w.dec_h; a.y = y;
+    st = hip_status(launch_decode(a, s, ev ? ev[3] : nullptr));
+    if (st == MOE_OK) st = record(ev, 4, s);
+    return st;
+  }
+
   st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, x, w.x16, d, s, ev);
   if (st != MOE_OK) return st;
 
@@ -226,18 +275,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   st = hip_status(launch_gemm(g2, kStoreH, true, s));
   if (st != MOE_OK) return st;
 
-  CombineArgs ca{};
-  ca.T = T;
-  ca.d = d;
-  ca.k = k;
-  ca.o = w.o;
-  ca.o_sh = fs > 0 ? w.o_sh : nullptr;
-  ca.pair_pos = rt.pair_pos;
-  ca.topk_w = rt.topk_w;
-  ca.y = y;
-  st = hip_status(launch_combine(ca, s));
-  if (st == MOE_OK) st = record(ev, 4, s);
-  return st;
+  return enqueue_combine(T, d, k, w.o, fs > 0 ? w.o_sh : nullptr, rt, y, s, ev);
 }
 
 }  // namespace

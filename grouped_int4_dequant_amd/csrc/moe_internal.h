@@ -93,4 +93,29 @@ struct GemmArgs {
 // otherwise bf16 in natural order, converted while staging.
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s);
 
+// ------------------------------------------------------------------ decode
+// Calls of at most kDecodeMaxT tokens run as two kernels (decode_kernels.hip):
+// gate/up with the routing repeated in every workgroup, then down with the
+// weighted combine. y is written directly.
+constexpr int kDecodeMaxT = 8;
+constexpr int kDecodeMaxPairs = 64;   // T * k
+constexpr int kDecodeMaxSlots = 12;   // k + 1 (waves of a down workgroup)
+
+struct DecodeArgs {
+  const float *logits;        // [T][E]
+  const uint16_t *x;          // bf16 [T][d]
+  int T, d, f, f_sh, E, k, fmax;
+  const uint32_t *gu_q; const uint16_t *gu_s, *gu_b; int64_t gu_qs, gu_ss;  // routed, per-expert strides
+  const uint32_t *dn_q; const uint16_t *dn_s, *dn_b; int64_t dn_qs, dn_ss;
+  const uint32_t *sh_gu_q; const uint16_t *sh_gu_s, *sh_gu_b;
+  const uint32_t *sh_dn_q; const uint16_t *sh_dn_s, *sh_dn_b;
+  int32_t *ids; float *gates; // [T][k], written by the gate/up kernel
+  float *h;                   // fp32 [T][k+1][fmax] (slot k: shared expert)
+  float *y;                   // fp32 [T][d]
+};
+
+bool decode_supported(int T, const moe_layer_t *L);
+// ev_mid (nullable) is recorded between the two kernels.
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_mid);
+
 }  // namespace moe

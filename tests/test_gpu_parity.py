@@ -170,6 +170,13 @@ EDGE_SHAPES = [
     (300, 512, 320, 12, 3, 192),
     (50, 2560, 192, 4, 2, 64),      # K = 2560: scale/bias table refilled after 2048 inputs
     (40, 448, 576, 5, 2, 0),        # 7 groups along d: scalar table fill
+    # persistent streaming GEMM (K a multiple of 512, at most 2048)
+    (40, 512, 512, 8, 2, 512),      # four steps per item, shared rows after routed rows
+    (250, 1024, 512, 3, 2, 0),      # experts split into several units, no shared expert
+    (130, 1536, 1024, 6, 2, 1024),  # 12 and 8 steps per item, partial last slice of d
+    (97, 512, 512, 1, 1, 512),      # one expert over 97 rows: two units
+    (192, 512, 512, 2, 1, 512),     # two full 96-row units per expert (six row blocks)
+    (60, 512, 512, 4, 2, 1024),     # shared width differs from f: general kernel
 ]
 
 
@@ -180,6 +187,17 @@ def test_layer_edge_shapes(moe, T, d, f, E, k, f_sh):
     y, routing = run_layer(moe, p)
     check_routing(routing, O.route(p.logits, k), T, k)
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"edge {T},{d},{f},{E},{k},{f_sh}")
+
+
+def test_layer_all_tokens_one_expert_set_streaming(moe):
+    """All tokens on the same two experts, at a shape the streaming GEMM takes."""
+    shape = S.LayerShape(d=512, f=512, E=16, k=2, f_sh=512)
+    p = S.make_custom(300, shape, seed=6)
+    p.logits[:, :2] += 100.0
+    say("all tokens -> experts {0,1}, streaming shape")
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, 2), 300, 2)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, 2), "one expert set (streaming)")
 
 
 def test_layer_all_tokens_one_expert_set(moe):
@@ -247,6 +265,39 @@ def test_decode_config4(moe, T):
             ys.append(y.cpu().numpy())
             refs.append(O.moe_forward(p.layer, p.x, p.logits, p.shape.k, weight_cache=cache))
     check_output(np.concatenate(ys), np.concatenate(refs), f"decode T={T}")
+
+
+DECODE_SHAPES = [
+    # T, E, k, f_sh  (d = 2048, f = 512: the two-kernel decode path)
+    (2, 256, 8, 512),
+    (3, 64, 4, 0),       # no shared expert, one key per lane
+    (8, 1024, 8, 512),   # 16 keys per lane, eight tokens
+    (5, 256, 1, 512),    # k = 1: gate 1
+    (8, 16, 8, 0),       # 64 picks over 16 experts: every expert shared by several tokens
+]
+
+
+@pytest.mark.parametrize("T,E,k,f_sh", DECODE_SHAPES)
+@pytest.mark.parametrize("with_routing", [False, True])
+def test_decode_shapes(moe, T, E, k, f_sh, with_routing):
+    p = S.make_custom(T, S.LayerShape(d=2048, f=512, E=E, k=k, f_sh=f_sh), seed=100 + T + E + k)
+    say(f"decode T={T} E={E} k={k} f_sh={f_sh} routing={'yes' if with_routing else 'no'}")
+    y, routing = run_layer(moe, p, with_routing=with_routing)
+    if with_routing:
+        check_routing(routing, O.route(p.logits, k), T, k)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"decode T={T} E={E} k={k}")
+
+
+def test_decode_tied_logits(moe):
+    """Exact ties (and -0.0 against +0.0) decide which experts the decode
+    kernels' own top-k picks; a wrong tie rule changes y by a whole expert."""
+    p = S.make_custom(4, S.LayerShape(d=2048, f=512, E=256, k=8, f_sh=512), seed=77)
+    p.logits[:] = np.round(p.logits * 2.0) / 2.0
+    p.logits[1, :] = 0.0
+    p.logits[1, 1::3] = -0.0
+    say("decode tied logits")
+    y, _ = run_layer(moe, p, with_routing=False)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, 8), "decode ties")
 
 
 def test_zero_tokens_is_a_noop(moe):
