@@ -42,51 +42,6 @@ constexpr int kSpan = 512;          // inputs per wave
 constexpr int kSteps = kSpan / 128;  // 128-input steps per wave
 constexpr int kMaxWaves = 8;         // gate/up waves per workgroup (d <= 4096)
 
-// Top-k of one token by one wave: lane j < k ends with the id and gate of
-// slot j (slots in descending logit order; gates = softmax over the k picks).
-// Each lane first sorts its own keys, so one round is a wave maximum over the
-// lanes' heads, after which the winning lane shifts its list up by one.
-template <int VPL>
-__device__ void topk_wave(const float *row, int E, int k, int lane, int &my_id, float &my_gate) {
-  uint64_t key[VPL];
-#pragma unroll
-  for (int r = 0; r < VPL; ++r) {
-    const int e = lane + 64 * r;
-    key[r] = e < E ? make_key(row[e], e) : 0ull;
-  }
-  // descending insertion sort of the lane's keys (VPL <= 16, unrolled)
-#pragma unroll
-  for (int i = 1; i < VPL; ++i)
-#pragma unroll
-    for (int j = i; j > 0; --j)
-      if (key[j] > key[j - 1]) {
-        const uint64_t t = key[j];
-        key[j] = key[j - 1];
-        key[j - 1] = t;
-      }
-  float v0 = 0.f, sum = 0.f, my_ex = 0.f;
-  my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    // wave maximum of the heads: first over the logit half of the key, then
-    // over the index half among the lanes that hold that logit
-    const uint32_t hi = (uint32_t)(key[0] >> 32);
-    const uint32_t mhi = wave_max32(hi);
-    const uint32_t lo = hi == mhi ? (uint32_t)key[0] : 0u;
-    const uint64_t win = ((uint64_t)mhi << 32) | wave_max32(lo);
-    if (key[0] == win) {  // keys are distinct: one lane wins and drops its head
-#pragma unroll
-      for (int r = 0; r + 1 < VPL; ++r) key[r] = key[r + 1];
-      key[VPL - 1] = 0ull;
-    }
-    const float wv = key_value(win);
-    if (j == 0) v0 = wv;
-    const float ex = expf(wv - v0);
-    sum += ex;
-    if (lane == j) { my_ex = ex; my_id = key_index(win); }
-  }
-  my_gate = my_ex / sum;
-}
-
 // Position of the r-th set bit of m (r < popcount(m)).
 __device__ __forceinline__ int nth_bit(uint32_t m, int r) {
   for (int i = 0; i < r; ++i) m &= m - 1;
@@ -320,22 +275,19 @@ bool decode_supported(int T, const moe_layer_t *L) {
          L->E <= MOE_MAX_EXPERTS;
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_mid) {
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start, hipEvent_t gu_stop,
+                         hipEvent_t dn_stop) {
   const int vpl = (a.E + 63) / 64;
   const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
-  if (vpl <= 1)       hipLaunchKernelGGL(decode_gu_kernel<1>, g1, b1, 0, s, a);
-  else if (vpl <= 2)  hipLaunchKernelGGL(decode_gu_kernel<2>, g1, b1, 0, s, a);
-  else if (vpl <= 4)  hipLaunchKernelGGL(decode_gu_kernel<4>, g1, b1, 0, s, a);
-  else if (vpl <= 8)  hipLaunchKernelGGL(decode_gu_kernel<8>, g1, b1, 0, s, a);
-  else                hipLaunchKernelGGL(decode_gu_kernel<16>, g1, b1, 0, s, a);
+  if (vpl <= 1)       hipExtLaunchKernelGGL(decode_gu_kernel<1>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
+  else if (vpl <= 2)  hipExtLaunchKernelGGL(decode_gu_kernel<2>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
+  else if (vpl <= 4)  hipExtLaunchKernelGGL(decode_gu_kernel<4>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
+  else if (vpl <= 8)  hipExtLaunchKernelGGL(decode_gu_kernel<8>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
+  else                hipExtLaunchKernelGGL(decode_gu_kernel<16>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (ev_mid) {
-    err = hipEventRecord(ev_mid, s);
-    if (err != hipSuccess) return err;
-  }
   const dim3 g2(a.T * (a.d / 16)), b2(64 * (a.k + 1));
-  hipLaunchKernelGGL(decode_dn_kernel, g2, b2, 0, s, a);
+  hipExtLaunchKernelGGL(decode_dn_kernel, g2, b2, 0, s, nullptr, dn_stop, 0, a);
   return hipGetLastError();
 }
 

@@ -464,18 +464,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop) {
   const dim3 grid(a.total_wg), block(kGemmThreads);
   if (a.total_wg == 0) return hipSuccess;
   if (a_f16) {
     switch (mode) {
-      case kSwiGLU: hipLaunchKernelGGL((gemm_kernel<kSwiGLU, true>), grid, block, 0, s, a); break;
-      case kStoreH: hipLaunchKernelGGL((gemm_kernel<kStoreH, true>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((gemm_kernel<kStoreC, true>), grid, block, 0, s, a); break;
+      case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true>), grid, block, 0, s, start, stop, 0, a); break;
+      case kStoreH: hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true>), grid, block, 0, s, start, stop, 0, a); break;
+      default: hipExtLaunchKernelGGL((gemm_kernel<kStoreC, true>), grid, block, 0, s, start, stop, 0, a); break;
     }
   } else {
     // bf16 activations: stand-alone GEMM over block-map entries (<= 32 rows)
-    hipLaunchKernelGGL((gemm_kernel<kStoreC, false>), grid, block, 0, s, a);
+    hipExtLaunchKernelGGL((gemm_kernel<kStoreC, false>), grid, block, 0, s, start, stop, 0, a);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;  // scan cost grows with (T/64)^2
+constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;
+constexpr int kMaxTopK = 64;  // one selected expert per lane of the top-k wave
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -41,6 +42,7 @@ int check_layer(const moe_layer_t *L) {
   if (!L) return MOE_EINVAL;
   if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->f_sh < 0) return MOE_EINVAL;
   if (L->k > L->E) return MOE_EINVAL;
+  if (L->k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (L->E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
   if (L->d % 64 || L->f % 64 || L->f_sh % 64) return MOE_EUNSUPPORTED;
   const void *req[] = {L->gu_q, L->gu_s, L->gu_b, L->dn_q, L->dn_s, L->dn_b};
@@ -66,6 +68,7 @@ int check_routing(const moe_routing_t *r) {
 struct Workspace {
   moe_routing_t rt;
   int32_t *units, *num_units;
+  int32_t *chunk_counts;
   uint16_t *x16, *h, *h_sh, *o, *o_sh;
   float *dec_h;  // decode-shape calls only
 };
@@ -87,6 +90,7 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.rt.num_blocks = c.take<int32_t>(1);
   o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E));
   o.num_units = c.take<int32_t>(1);
+  o.chunk_counts = c.take<int32_t>((size_t)ceil_div(T, kSubChunk) * E);
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
   // The shared expert's rows follow the routed rows in h and o when their
   // widths match, so one grouped GEMM can cover both.
@@ -106,7 +110,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
-                  int32_t *units, int32_t *num_units, const uint16_t *x,
+                  int32_t *chunk_counts, int32_t *units, int32_t *num_units, const uint16_t *x,
                   uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
   TopkArgs ta{};
   ta.logits = logits;
@@ -118,9 +122,8 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   ta.x = x;
   ta.x16 = x16;
   ta.d = d;
-  hipError_t err = launch_topk(ta, s);
+  hipError_t err = launch_topk(ta, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   if (err != hipSuccess) return MOE_EHIP;
-  if (record(ev, 1, s) != MOE_OK) return MOE_EHIP;
 
   ScanArgs sa{};
   sa.T = T;
@@ -136,11 +139,10 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   sa.num_blocks = rt.num_blocks;
   sa.max_blocks = moe_max_blocks(T, E, k);
   sa.units = units;
+  sa.chunk_counts = chunk_counts;
   sa.num_units = num_units;
   sa.max_units = units ? (int)max_units_routed(T, k, E) : 0;
-  int st = hip_status(launch_scan(sa, s));
-  if (st == MOE_OK) st = record(ev, 2, s);
-  return st;
+  return hip_status(launch_scan(sa, s, ev ? ev[2] : nullptr));
 }
 
 // Workgroups of one grouped problem: units rounded up to a multiple of 8 (one
@@ -162,9 +164,7 @@ int enqueue_combine(int T, int d, int k, const uint16_t *o, const uint16_t *o_sh
   ca.pair_pos = rt.pair_pos;
   ca.topk_w = rt.topk_w;
   ca.y = y;
-  int st = hip_status(launch_combine(ca, s));
-  if (st == MOE_OK) st = record(ev, 4, s);
-  return st;
+  return hip_status(launch_combine(ca, s, ev ? ev[4] : nullptr));
 }
 
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
@@ -177,17 +177,14 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   const moe_routing_t &rt = routing ? *routing : w.rt;
   const int d = L->d, f = L->f, E = L->E, k = L->k, fs = L->f_sh;
 
-  int st = record(ev, 0, s);
-  if (st != MOE_OK) return st;
-
+  int st = MOE_OK;
   if (decode_supported(T, L)) {
     // A few tokens: gate/up (routing repeated inside) and down + combine.
     // Routing tensors are produced by the routing kernels only when asked for.
     if (routing) {
-      st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, nullptr, nullptr, d, s, ev);
+      st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, nullptr, nullptr, d, s, ev);
     } else {
-      st = record(ev, 1, s);
-      if (st == MOE_OK) st = record(ev, 2, s);
+      for (int i = 0; i < 2 && st == MOE_OK; ++i) st = record(ev, i, s);  // no routing kernels
     }
     if (st != MOE_OK) return st;
     DecodeArgs a{};
@@ -201,12 +198,11 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     a.sh_dn_q = L->sh_dn_q; a.sh_dn_s = L->sh_dn_s; a.sh_dn_b = L->sh_dn_b;
     a.ids = w.rt.topk_ids; a.gates = w.rt.topk_w;  // the workspace's own routing buffers
     a.h = w.dec_h; a.y = y;
-    st = hip_status(launch_decode(a, s, ev ? ev[3] : nullptr));
-    if (st == MOE_OK) st = record(ev, 4, s);
-    return st;
+    hipEvent_t gu_start = (ev && !routing) ? ev[2] : nullptr;
+    return hip_status(launch_decode(a, s, gu_start, ev ? ev[3] : nullptr, ev ? ev[4] : nullptr));
   }
 
-  st = enqueue_route(logits, T, E, k, rt, w.units, w.num_units, x, w.x16, d, s, ev);
+  st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev);
   if (st != MOE_OK) return st;
 
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
@@ -238,8 +234,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   }
   g1.nprob = np;
   g1.total_wg = nwg;
-  st = hip_status(launch_gemm(g1, kSwiGLU, true, s));
-  if (st == MOE_OK) st = record(ev, 3, s);
+  st = hip_status(launch_gemm(g1, kSwiGLU, true, s, nullptr, ev ? ev[3] : nullptr));
   if (st != MOE_OK) return st;
 
   // down projection into fp16 expert outputs, then the weighted combine
@@ -289,26 +284,27 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k) {
 
 size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
   if (T < 0 || E <= 0 || E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return 0;
-  return kAlign;  // routing keeps its scratch in LDS; the argument is reserved
+  // per-sub-chunk expert counts
+  return (size_t)round_up(std::max<int64_t>(ceil_div(T, kSubChunk), 1) * E * (int64_t)sizeof(int32_t), kAlign);
 }
 
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {
   if (!L || T < 0 || T > kMaxRouteTokens) return 0;
   if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->k > L->E || L->f_sh < 0) return 0;
-  if (L->E > MOE_MAX_EXPERTS || L->d % 64 || L->f % 64 || L->f_sh % 64) return 0;
+  if (L->E > MOE_MAX_EXPERTS || L->k > kMaxTopK || L->d % 64 || L->f % 64 || L->f_sh % 64) return 0;
   return carve_layer(T, L, nullptr, nullptr);
 }
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_routing_t *out,
               void *ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;
-  if (E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || T > kMaxRouteTokens || k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (check_routing(out) != MOE_OK) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
-  if (!logits) return MOE_EINVAL;
-  (void)ws;
-  (void)ws_bytes;
-  return enqueue_route(logits, T, E, k, *out, nullptr, nullptr, nullptr, nullptr, 0, stream);
+  if (!logits || !ws || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  if (ws_bytes < moe_route_workspace_bytes(T, E)) return MOE_EWORKSPACE;
+  return enqueue_route(logits, T, E, k, *out, static_cast<int32_t *>(ws), nullptr, nullptr, nullptr, nullptr, 0,
+                       stream);
 }
 
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, int32_t N,

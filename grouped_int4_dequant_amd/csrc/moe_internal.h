@@ -3,6 +3,7 @@
 // the public interface is include/moe_int4.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,11 +50,15 @@ struct ScanArgs {
   int max_blocks;
   int32_t *units, *num_units;   // optional GEMM work list (nullptr: none)
   int max_units;
+  int32_t *chunk_counts;        // scratch [ceil(T/64)][E]
 };
 
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+// Optional events (nullable) are attached to a kernel's dispatch: start at
+// its first wave, stop at its end, with no extra packet between kernels.
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s, hipEvent_t stop = nullptr);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s, hipEvent_t stop = nullptr);
 
 // --------------------------------------------------------------- grouped GEMM
 // Epilogue modes of the grouped GEMM kernel.
@@ -91,7 +96,8 @@ struct GemmArgs {
 
 // a_f16: the A operand is fp16 in the permuted-run layout (fast path);
 // otherwise bf16 in natural order, converted while staging.
-hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 // ------------------------------------------------------------------ decode
 // Calls of at most kDecodeMaxT tokens run as two kernels (decode_kernels.hip):
@@ -115,7 +121,8 @@ struct DecodeArgs {
 };
 
 bool decode_supported(int T, const moe_layer_t *L);
-// ev_mid (nullable) is recorded between the two kernels.
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t ev_mid);
+// gu_start, gu_stop, dn_stop (nullable): dispatch events of the two kernels.
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start, hipEvent_t gu_stop,
+                         hipEvent_t dn_stop);
 
 }  // namespace moe

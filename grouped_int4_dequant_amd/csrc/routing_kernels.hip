@@ -10,14 +10,17 @@
 //   topk  one wave per token. Every candidate becomes a 64-bit key
 //         (order-preserving logit bits, then the inverted expert index), so
 //         "larger logit, then lower index" is plain unsigned order and all
-//         keys are distinct. k rounds of a wave max (DPP inside each 16-lane
-//         row, readlane across rows) pick the experts; the gates are the
-//         softmax over the k picked logits. The same workgroups then convert
-//         x to fp16 for the GEMMs.
-//   scan  one workgroup per 64-token sub-chunk c. Each rebuilds, in LDS, the
-//         per-expert totals, the counts of tokens before its sub-chunk and a
-//         64-bit token mask per expert for its own sub-chunk, scans the totals
-//         into offsets and scatters its pairs stably:
+//         keys are distinct. Each lane sorts its own keys; k rounds of a wave
+//         max over the lanes' heads (DPP inside each 16-lane row, readlane
+//         across rows, the logit half first, then the index half) pick the
+//         experts; the gates are the softmax over the k picked logits. The
+//         same workgroups then convert x to fp16 for the GEMMs.
+//   count one workgroup per 64-token sub-chunk c: per-expert counts of its
+//         pairs, cnt[c][e].
+//   scan  one workgroup per sub-chunk: column sums of cnt give the expert
+//         totals and the counts before its sub-chunk, an exclusive scan over
+//         experts gives the offsets, and a 64-bit token mask per expert for
+//         its own sub-chunk gives the stable scatter:
 //           pos = offset[e] + before[e] + popcount(mask[e] & tokens below t).
 //         Integer atomics commute, so the result is deterministic.
 //         Workgroup 0 also writes counts, offsets, the 32-row block map and
@@ -45,34 +48,12 @@ constexpr int kMaxVpl = MOE_MAX_EXPERTS / kWave;  // logits per lane at E = 1024
 
 template <int VPL>
 __device__ void route_token(const TopkArgs &a, int t, int lane) {
-  const int E = a.E, k = a.k;
-  const float *row = a.logits + (int64_t)t * E;
-  uint64_t key[VPL];
-#pragma unroll
-  for (int r = 0; r < VPL; ++r) {
-    const int e = lane + kWave * r;
-    key[r] = e < E ? make_key(row[e], e) : 0ull;
-  }
-  uint32_t taken = 0;
-  float v0 = 0.f, sum = 0.f, my_ex = 0.f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0ull;
-    int br = 0;
-#pragma unroll
-    for (int r = 0; r < VPL; ++r)
-      if (!((taken >> r) & 1u) && key[r] > best) { best = key[r]; br = r; }
-    const uint64_t win = wave_max64(best);
-    if (best == win) taken |= 1u << br;  // keys are distinct: one lane wins
-    const float wv = key_value(win);
-    if (j == 0) v0 = wv;
-    const float ex = expf(wv - v0);
-    sum += ex;  // every lane accumulates the same sum, slot order
-    if (lane == j) { my_ex = ex; my_id = key_index(win); }
-  }
-  if (lane < k) {
-    a.topk_ids[(int64_t)t * k + lane] = my_id;
-    a.topk_w[(int64_t)t * k + lane] = my_ex / sum;
+  int id;
+  float g;
+  topk_wave<VPL>(a.logits + (int64_t)t * a.E, a.E, a.k, lane, id, g);
+  if (lane < a.k) {
+    a.topk_ids[(int64_t)t * a.k + lane] = id;
+    a.topk_w[(int64_t)t * a.k + lane] = g;
   }
 }
 
@@ -171,7 +152,28 @@ __device__ int block_exclusive_scan(int *vals, int n, int *scratch) {
   return total;
 }
 
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
+// Per 64-token sub-chunk c: how many of its (token, slot) pairs pick each
+// expert, into cnt[c][e].
+__global__ __launch_bounds__(kThreads) void count_kernel(ScanArgs a) {
+  __shared__ int s_cnt[MOE_MAX_EXPERTS];
+  const int E = a.E, k = a.k;
+  const int c = blockIdx.x;
+  const int64_t tk = (int64_t)a.T * k;
+  const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
+  for (int e = threadIdx.x; e < E; e += kThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads) atomicAdd(&s_cnt[a.topk_ids[idx]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) a.chunk_counts[(int64_t)c * E + e] = s_cnt[e];
+}
+
+// Per sub-chunk c: expert totals and the counts of the sub-chunks before c
+// (column sums of cnt), offsets by an exclusive scan over experts, and the
+// stable scatter of c's pairs:
+//   pos = offset[e] + before[e] + popcount(mask[e] & tokens of c below t).
+// Workgroup 0 also writes counts, offsets, the 32-row block map and the GEMM
+// work list.
+__global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS];
@@ -179,40 +181,31 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ int s_scratch[kWaves];
   const int E = a.E, k = a.k, T = a.T;
-  const int c = blockIdx.x;
+  const int c = blockIdx.x, C = gridDim.x;
   const int64_t tk = (int64_t)T * k;
-  const int64_t lo = (int64_t)c * kSubChunk * k;
-  const int64_t hi = min(tk, lo + (int64_t)kSubChunk * k);
+  const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
 
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    s_tot[e] = 0;
-    s_pre[e] = 0;
+    int tot = 0, pre = 0;
+    for (int c0 = 0; c0 < C; c0 += 16) {  // sixteen independent loads in flight
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? a.chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        tot += v[u];
+        pre += c0 + u < c ? v[u] : 0;
+      }
+    }
+    s_tot[e] = tot;
+    s_pre[e] = pre;
+    s_off[e] = tot;
     s_mask[e] = 0ull;
   }
   __syncthreads();
-  // loads are batched (kBatch independent loads in flight per thread)
-  constexpr int kBatch = 16;
-  for (int64_t base = threadIdx.x; base < tk; base += (int64_t)kThreads * kBatch) {
-    int ids[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t idx = base + (int64_t)u * kThreads;
-      ids[u] = idx < tk ? a.topk_ids[idx] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t idx = base + (int64_t)u * kThreads;
-      const int e = ids[u];
-      if (e < 0) continue;
-      atomicAdd(&s_tot[e], 1);
-      if (idx < lo) atomicAdd(&s_pre[e], 1);
-      else if (idx < hi) atomicOr(&s_mask[e], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) s_off[e] = s_tot[e];
-  __syncthreads();
-  const int total = block_exclusive_scan(s_off, E, s_scratch);  // == T*k
+  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads)
+    atomicOr(&s_mask[a.topk_ids[idx]], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+  const int total = block_exclusive_scan(s_off, E, s_scratch);  // == T*k (syncs inside)
 
   // stable scatter of this sub-chunk's (token, slot) pairs
   for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads) {
@@ -274,28 +267,31 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int vpl = (a.E + kWave - 1) / kWave;
   int nwg = (int)ceil_div(a.T, kWaves);
   if (a.x16) nwg = (int)std::max<int64_t>(nwg, std::min<int64_t>(1024, ceil_div((int64_t)a.T * a.d / 8, 4 * kThreads)));
   nwg = std::min(nwg, 4096);
   const dim3 grid(nwg), block(kThreads);
-  if (vpl <= 1)       hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, a);
-  else if (vpl <= 2)  hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
-  else if (vpl <= 4)  hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
-  else if (vpl <= 8)  hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
-  else                hipLaunchKernelGGL(topk_kernel<kMaxVpl>, grid, block, 0, s, a);
+  if (vpl <= 1)       hipExtLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, start, stop, 0, a);
+  else if (vpl <= 2)  hipExtLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, start, stop, 0, a);
+  else if (vpl <= 4)  hipExtLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, start, stop, 0, a);
+  else if (vpl <= 8)  hipExtLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, start, stop, 0, a);
+  else                hipExtLaunchKernelGGL(topk_kernel<kMaxVpl>, grid, block, 0, s, start, stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(kThreads), 0, s, a);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s, hipEvent_t stop) {
+  hipExtLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(kThreads), 0, s, nullptr, stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s, hipEvent_t stop) {
   const int C = (int)ceil_div(a.T, kSubChunk);
-  hipLaunchKernelGGL(scan_kernel, dim3(C), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(count_kernel, dim3(C), dim3(kThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipExtLaunchKernelGGL(scatter_kernel, dim3(C), dim3(kThreads), 0, s, nullptr, stop, 0, a);
   return hipGetLastError();
 }
 

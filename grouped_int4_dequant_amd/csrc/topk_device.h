@@ -64,4 +64,49 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
 }
 
 
+// Top-k of one token by one wave: lane j < k ends with the id and gate of
+// slot j (slots in descending logit order; gates = softmax over the k picks).
+// Each lane first sorts its own keys, so one round is a wave maximum over the
+// lanes' heads, after which the winning lane shifts its list up by one.
+template <int VPL>
+__device__ __forceinline__ void topk_wave(const float *row, int E, int k, int lane, int &my_id, float &my_gate) {
+  uint64_t key[VPL];
+#pragma unroll
+  for (int r = 0; r < VPL; ++r) {
+    const int e = lane + 64 * r;
+    key[r] = e < E ? make_key(row[e], e) : 0ull;
+  }
+  // descending insertion sort of the lane's keys (VPL <= 16, unrolled)
+#pragma unroll
+  for (int i = 1; i < VPL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j)
+      if (key[j] > key[j - 1]) {
+        const uint64_t t = key[j];
+        key[j] = key[j - 1];
+        key[j - 1] = t;
+      }
+  float v0 = 0.f, sum = 0.f, my_ex = 0.f;
+  my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    // wave maximum of the heads: first over the logit half of the key, then
+    // over the index half among the lanes that hold that logit
+    const uint32_t hi = (uint32_t)(key[0] >> 32);
+    const uint32_t mhi = wave_max32(hi);
+    const uint32_t lo = hi == mhi ? (uint32_t)key[0] : 0u;
+    const uint64_t win = ((uint64_t)mhi << 32) | wave_max32(lo);
+    if (key[0] == win) {  // keys are distinct: one lane wins and drops its head
+#pragma unroll
+      for (int r = 0; r + 1 < VPL; ++r) key[r] = key[r + 1];
+      key[VPL - 1] = 0ull;
+    }
+    const float wv = key_value(win);
+    if (j == 0) v0 = wv;
+    const float ex = expf(wv - v0);
+    sum += ex;
+    if (lane == j) { my_ex = ex; my_id = key_index(win); }
+  }
+  my_gate = my_ex / sum;
+}
+
 }  // namespace moe

@@ -130,16 +130,21 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
  */
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L);
 
-/* Bytes of device workspace moe_route accepts (routing keeps its scratch in
- * LDS; the workspace arguments of moe_route are reserved and may be null). */
+/* Bytes of device workspace moe_route needs for T tokens over E experts (the
+ * per-64-token expert counts; 32 KiB at T=2048, E=256). Host-only; 0 on
+ * invalid arguments. */
 size_t moe_route_workspace_bytes(int32_t T, int32_t E);
 
 /*
  * Routing only. logits fp32 [T][E] (device). Fills every field of *out (the
  * struct itself is read on the host; its pointers are device pointers).
- * Errors: MOE_EINVAL (null, T < 0, k < 1, k > E), MOE_EUNSUPPORTED
- * (E > 1024, T > MOE_MAX_CALL_TOKENS). T == 0 enqueues nothing. Launches
- * two kernels (top-k, then histogram/scan/scatter/block map).
+ * ws: device workspace of at least moe_route_workspace_bytes(T, E) bytes,
+ * 256-byte aligned (its contents need not be initialised).
+ * Errors: MOE_EINVAL (null, unaligned ws, T < 0, k < 1, k > E),
+ * MOE_EUNSUPPORTED (E > 1024, k > 64, T > MOE_MAX_CALL_TOKENS),
+ * MOE_EWORKSPACE (ws_bytes too small). T == 0 enqueues nothing. Launches
+ * three kernels (top-k; per-64-token expert counts; offsets, stable scatter
+ * and block map).
  */
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
               const moe_routing_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -173,22 +178,35 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
  * x bf16 [T][d]; logits fp32 [T][E]; y fp32 [T][d], fully overwritten.
  * routing: optional (may be NULL); when given, it receives the routing
  * tensors of this call. ws: device workspace of at least
- * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Enqueues five kernels
- * (top-k, scan/scatter, gate-up, down, combine) and never synchronises.
- * The combine adds the k weighted expert rows in slot order and then the
- * shared expert's row, in fp32, so y is reproducible bit for bit.
- * T == 0 enqueues nothing.
+ * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Never synchronises.
+ * Prefill enqueues six kernels (top-k, per-64-token counts, scan/scatter,
+ * gate-up, down, combine). Calls of at most 8 tokens with d a multiple of
+ * 512, f == 512 and f_sh in {0, 512} take the decode form instead: two
+ * kernels (gate-up with the top-k repeated in each workgroup; down with
+ * the combine), plus the routing kernels only when routing is requested
+ * (Lily-EN "Decode: Minimize Bytes Moved Per Token": decode is bound by the
+ * bytes of the touched experts). Either way the k weighted expert rows are
+ * added in slot order and then the shared expert's row, in fp32, so y is
+ * reproducible bit for bit. T == 0 enqueues nothing.
+ * Errors: MOE_EINVAL (null or misaligned pointer, T < 0, k > E),
+ * MOE_EUNSUPPORTED (E > 1024, k > 64, d/f/f_sh not multiples of 64,
+ * T > MOE_MAX_CALL_TOKENS), MOE_EWORKSPACE, MOE_EHIP.
  */
 int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
                       float *y, const moe_routing_t *routing,
                       void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_layer_forward with stage timing, for measurement: records events[0]
- * before the first kernel and events[1..4] after the top-k, scan/scatter,
- * gate-up and down(+combine) kernels, all on `stream`. events: 5 caller-created
- * hipEvent_t handles (host array). Requires T >= 1; otherwise as
- * moe_layer_forward.
+ * moe_layer_forward with stage timing, for measurement. The events are
+ * attached to the kernel dispatches themselves (no marker packets between
+ * kernels, so timing adds no idle time): events[0] at the start of the top-k
+ * kernel, events[1] at its end, events[2] at the end of the count/scatter
+ * kernels, events[3] at the end of the gate/up kernel and events[4] at the end
+ * of the last kernel (down + combine). In the few-token form without routing
+ * outputs there are no routing kernels: events[0] and events[1] are recorded
+ * as markers and events[2] is the start of the gate/up kernel. events: 5
+ * caller-created hipEvent_t handles (host array). Requires T >= 1; otherwise
+ * as moe_layer_forward.
  */
 int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float *logits,
                             int32_t T, float *y, const moe_routing_t *routing,

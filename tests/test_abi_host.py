@@ -97,6 +97,11 @@ def test_route_and_gemm_reject_bad_arguments():
     assert lib.moe_route(0x1000, 64, 2048, 8, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EUNSUPPORTED
     assert lib.moe_route(0x1000, 0, 16, 2, ctypes.byref(r), None, 0, None) == B.MOE_OK  # T == 0
     assert lib.moe_route(None, 64, 16, 2, ctypes.byref(r), None, 0, None) == B.MOE_EINVAL
+    assert lib.moe_route(0x1000, 64, 256, 65, ctypes.byref(r), 0x1000, 1 << 20, None) == B.MOE_EUNSUPPORTED
+    need = lib.moe_route_workspace_bytes(64, 16)
+    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r), 0x1000, need - 1, None) == B.MOE_EWORKSPACE
+    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r), None, need, None) == B.MOE_EINVAL
+    assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r), 0x1010, need, None) == B.MOE_EINVAL  # unaligned
     r0 = B.MoeRoutingT(*([0x1000] * 8 + [None]))
     assert lib.moe_route(0x1000, 64, 16, 2, ctypes.byref(r0), 0x1000, 1 << 20, None) == B.MOE_EINVAL
     g = lib.moe_grouped_gemm_int4
