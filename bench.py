@@ -37,9 +37,9 @@ METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak
 TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "7476d7b702e0a083b1e27a5904f20bb33299aaf57899ba81d9388a0be5acf4e2"
-TRAFFIC_BYTES = {"gate_up": (190745.7 * 2.0 + 18434.0) * 1024,
-                 "down_combine": (85988.7 * 2.0 + 73728.0 + 37137.1 * 2.0 + 16384.1) * 1024}
+TRAFFIC_DIGEST = "7b1080532bd3916c4c555bd1df8a43d69697fc12734678b4a9156718b485925c"
+TRAFFIC_BYTES = {"gate_up": (183304.2 * 2.0 + 18432.3) * 1024,
+                 "down_combine": (85870.0 * 2.0 + 73728.0 + 37132.6 * 2.0 + 16384.2) * 1024}
 
 
 def sources_digest():

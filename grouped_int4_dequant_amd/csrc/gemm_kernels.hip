@@ -48,6 +48,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -162,6 +164,11 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint16_t *wsc = P.Ws + (int64_t)U.e * P.ws_estride;
   const uint16_t *wbi = P.Wb + (int64_t)U.e * P.ws_estride;
   const int kw = K >> 3;
+  // code-word offset of each column block's weight row within the expert
+  // (the host keeps one expert's N * K / 8 words below 2^31)
+  uint32_t b_row[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) b_row[cb] = (uint32_t)ncol[cb] * (uint32_t)kw;
 
   // first input of this lane's quarter at step s (valid iff < K)
   auto lane_k0 = [&](int s) { return kKStep * s + 32 * kq; };
@@ -171,7 +178,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     const int kc = k0 < K ? k0 : 0;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
-      st.q[cb] = *reinterpret_cast<const u4 *>(wq + (int64_t)ncol[cb] * kw + (kc >> 3));
+      st.q[cb] = *reinterpret_cast<const u4 *>(wq + (uint32_t)(b_row[cb] + (kc >> 3)));
   };
 
   // Scale/bias table for groups [32 gc, 32 gc + 32): tab[g][c] holds
@@ -227,20 +234,25 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // rows. bf16 activations are converted to fp16 on the way.
   // Per slab of this wave: the activation row and the 16-byte chunk this lane
   // moves, fixed for the whole unit; only the K offset changes per step.
-  const uint16_t *a_row_ptr[kSlabs];
+  // element offset of the activation row and this lane's 16-byte chunk: 32
+  // bits for fp16 activations (the layer's own buffers, whose size the host
+  // bounds), 64 bits for a caller's bf16 matrix
+  typedef typename std::conditional<AF16, uint32_t, uint64_t>::type AOff;
+  const uint16_t *a_base = reinterpret_cast<const uint16_t *>(P.A);
+  AOff a_row_off[kSlabs];
   int a_q32[kSlabs], a_in[kSlabs];
 #pragma unroll
   for (int ii = 0; ii < kSlabs; ++ii) {
     const int r = kSlabRows * (wave + kWaves * ii) + (lane >> 4);
     const int ch = (lane & 15) ^ (r & 15);
-    a_row_ptr[ii] = reinterpret_cast<const uint16_t *>(P.A) + (int64_t)s_arow[min(r, nr - 1)] * P.lda;
+    a_row_off[ii] = (AOff)s_arow[min(r, nr - 1)] * (AOff)P.lda;
     a_q32[ii] = 32 * (ch >> 2);
     a_in[ii] = 32 * (ch >> 2) + 8 * (ch & 3);
   }
   auto a_src = [&](int s, int ii) {
     const int off = kKStep * s;
     const int kel = off + a_q32[ii] < K ? off + a_in[ii] : 0;
-    return a_row_ptr[ii] + kel;
+    return a_base + (a_row_off[ii] + (AOff)kel);
   };
 
   uint4 a_regs[kSlabs];

@@ -176,6 +176,12 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   carve_layer(T, L, static_cast<char *>(ws), &w);
   const moe_routing_t &rt = routing ? *routing : w.rt;
   const int d = L->d, f = L->f, E = L->E, k = L->k, fs = L->f_sh;
+  // The GEMM addresses the layer's fp16 activation buffers and one expert's
+  // codes with 32-bit offsets.
+  const int64_t wmax = std::max<int64_t>(f, fs);
+  if ((int64_t)T * (k + 1) * wmax >= (1LL << 31) || (int64_t)T * d >= (1LL << 31) ||
+      2 * wmax * d / 8 >= (1LL << 31))
+    return MOE_EUNSUPPORTED;
 
   int st = MOE_OK;
   if (decode_supported(T, L)) {
@@ -314,6 +320,7 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, 
   if (!A || !Wq || !Ws || !Wb || !block_map || !num_blocks || !C) return MOE_EINVAL;
   if (N <= 0 || K <= 0 || max_blocks < 0 || lda < K || ldc < N) return MOE_EINVAL;
   if (N % 64 || K % 64) return MOE_EUNSUPPORTED;
+  if ((int64_t)N * (K / 8) >= (1LL << 31)) return MOE_EUNSUPPORTED;  // 32-bit code offsets
   if (!aligned16(A) || lda % 8 || !aligned16(Wq) || !aligned16(Ws) || !aligned16(Wb))
     return MOE_EINVAL;
   if (max_blocks == 0) return MOE_OK;

@@ -45,6 +45,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxVpl = MOE_MAX_EXPERTS / kWave;  // logits per lane at E = 1024
+constexpr int kClasses = kUnitRows / 16;           // GEMM unit size classes (16-row blocks)
 
 template <int VPL>
 __device__ void route_token(const TopkArgs &a, int t, int lane) {
@@ -247,22 +248,43 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   if (threadIdx.x == 0) *a.num_blocks = nblocks;
   if (a.units == nullptr) return;
   __syncthreads();
-  // work list: each expert's rows split evenly into ceil(rows / kUnitRows) units
-  for (int e = threadIdx.x; e < E; e += kThreads) s_aux[e] = (s_tot[e] + kUnitRows - 1) / kUnitRows;
+  // Work list: each expert's rows split evenly into ceil(rows / kUnitRows)
+  // units, listed by 16-row size class, largest first, so the GEMM (which
+  // hands units to workgroups in list order) starts the longest ones first.
+  // The order within a class follows LDS atomics; it changes which
+  // workgroup runs a unit, never a result.
+  __shared__ int s_cls[kClasses + 1];
+  if (threadIdx.x <= kClasses) s_cls[threadIdx.x] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) s_pre[e] = s_aux[e];  // units per expert
-  const int nunits = block_exclusive_scan(s_aux, E, s_scratch);
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = s_pre[e];
+    const int tot = s_tot[e], nu = (tot + kUnitRows - 1) / kUnitRows;
+    for (int u = 0; u < nu; ++u) {
+      const int rows = (int)((int64_t)(u + 1) * tot / nu) - (int)((int64_t)u * tot / nu);
+      atomicAdd(&s_cls[kClasses - (rows + 15) / 16], 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i <= kClasses; ++i) {
+      const int n = s_cls[i];
+      s_cls[i] = run;
+      run += n;
+    }
+    *a.num_units = run;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int tot = s_tot[e], nu = (tot + kUnitRows - 1) / kUnitRows;
     for (int u = 0; u < nu; ++u) {
       const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
-      int32_t *ent = a.units + 3 * (int64_t)(s_aux[e] + u);
+      const int slot = atomicAdd(&s_cls[kClasses - (b1 - b0 + 15) / 16], 1);
+      int32_t *ent = a.units + 3 * (int64_t)slot;
       ent[0] = e;
       ent[1] = s_off[e] + b0;
       ent[2] = b1 - b0;
     }
   }
-  if (threadIdx.x == 0) *a.num_units = nunits;
 }
 
 }  // namespace

@@ -162,9 +162,9 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
  *   Wq        uint32 [G][N][K/8]; Ws, Wb bf16 [G][N][K/64]; 16-byte aligned
  *   block_map int32 [max_blocks][3] as produced by moe_route; num_blocks [1]
  *   C         fp32 [*][ldc]; rows not covered by a block are not written
- * N and K must be multiples of 64; every block has 1..32 rows (the block
- * map contract; longer blocks are cut at 96 rows). Each block is one work
- * unit of the kernel.
+ * N and K must be multiples of 64 (else MOE_EUNSUPPORTED, as is N * K / 8
+ * reaching 2^31); every block has 1..32 rows (the block map contract; longer
+ * blocks are cut at 96 rows). Each block is one work unit of the kernel.
  */
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
                           int32_t N, int32_t K,
@@ -190,7 +190,9 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
  * reproducible bit for bit. T == 0 enqueues nothing.
  * Errors: MOE_EINVAL (null or misaligned pointer, T < 0, k > E),
  * MOE_EUNSUPPORTED (E > 1024, k > 64, d/f/f_sh not multiples of 64,
- * T > MOE_MAX_CALL_TOKENS), MOE_EWORKSPACE, MOE_EHIP.
+ * T > MOE_MAX_CALL_TOKENS, or a layer so large that T * (k + 1) * max(f, f_sh),
+ * T * d or one expert's 2 * max(f, f_sh) * d / 8 code words reach 2^31),
+ * MOE_EWORKSPACE, MOE_EHIP.
  */
 int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
                       float *y, const moe_routing_t *routing,
