@@ -59,13 +59,14 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kGemmThreads / 64;
-constexpr int kCB = 4;                            // 16-column MFMA blocks per wave
+constexpr int kCols = 512;                        // weight rows (output columns) per workgroup
+constexpr int kCB = kCols / (16 * kWaves);        // 16-column MFMA blocks per wave
+constexpr int kHalf = kCB / 2;                    // gate blocks (then as many up blocks) in SwiGLU mode
 constexpr int kKStep = 128;                       // K per step (4 quarters x 32)
 constexpr int kRowBytes = kKStep * 2;             // one row of one step in LDS (fp16)
 constexpr int kBufBytes = kUnitRows * kRowBytes;  // one step of a full unit (24 KiB)
 constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 
-constexpr int kCols = kWaves * 64;                // weight rows (output columns) per workgroup
 constexpr int kTabGroups = 32;                     // scale/bias groups held at a time (2048 inputs)
 constexpr int kTabStride = kCols + 16;             // dwords per group row of the table (padded)
 
@@ -128,13 +129,13 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   int ncol[kCB];
   bool active;
   if (MODE == kSwiGLU) {
-    const int f = N >> 1, ng = U.slice * 256 + wave * 32;
+    const int f = N >> 1, ng = U.slice * (kCols / 2) + wave * 8 * kCB;
     active = ng < f;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
-      ncol[cb] = (cb < 2 ? ng + 16 * cb : f + ng + 16 * (cb - 2)) + c16;
+      ncol[cb] = (cb < kHalf ? ng + 16 * cb : f + ng + 16 * (cb - kHalf)) + c16;
   } else {
-    const int n0 = U.slice * 512 + wave * 64;
+    const int n0 = U.slice * kCols + wave * 16 * kCB;
     active = n0 < N;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) ncol[cb] = n0 + 16 * cb + c16;
@@ -149,8 +150,8 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   int tcol[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb)
-    tcol[cb] = (MODE == kSwiGLU ? (cb < 2 ? 32 * wave + 16 * cb : kCols / 2 + 32 * wave + 16 * (cb - 2))
-                                : 64 * wave + 16 * cb) + c16;
+    tcol[cb] = (MODE == kSwiGLU ? (cb < kHalf ? 8 * kCB * wave + 16 * cb : kCols / 2 + 8 * kCB * wave + 16 * (cb - kHalf))
+                                : 16 * kCB * wave + 16 * cb) + c16;
   auto tab_row = [&](int c) -> int {
     if (MODE == kSwiGLU) {
       const int f = N >> 1, n = U.slice * (kCols / 2) + (c & (kCols / 2 - 1));
@@ -388,17 +389,17 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // accumulator element i of lane (c16, kq) in block (rb, cb) is row
   // 16*rb + 4*kq + i, column 16*cb + c16 of the wave's tile
   if (MODE == kSwiGLU) {
-    const int ng = U.slice * 256 + wave * 32;
+    const int ng = U.slice * (kCols / 2) + wave * 8 * kCB;
 #pragma unroll
     for (int rb = 0; rb < kMaxRB; ++rb) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < kHalf; ++cb) {
         const int col = perm_col(ng + 16 * cb + c16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rb + 4 * kq + i;
           if (r < nr) {
-            const float g = acc[rb][cb][i], u = acc[rb][cb + 2][i];
+            const float g = acc[rb][cb][i], u = acc[rb][cb + kHalf][i];
             const float h = g / (1.f + __expf(-g)) * u;
             P.H[(int64_t)(U.r0 + r) * P.ldh + col] = f32_to_f16_bits(h);
           }
@@ -406,7 +407,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
       }
     }
   } else {
-    const int n0 = U.slice * 512 + wave * 64;
+    const int n0 = U.slice * kCols + wave * 16 * kCB;
 #pragma unroll
     for (int rb = 0; rb < kMaxRB; ++rb) {
 #pragma unroll
