@@ -14,7 +14,10 @@
 //     SIMD, at most 256 registers per lane); a wave owns 64 weight rows
 //     (output columns) as four 16-column MFMA blocks and every row of the
 //     unit, so each rebuilt weight feeds every row of the unit, and the
-//     unit's activation rows are staged once for 512 columns.
+//     unit's activation rows are staged once for 512 columns. Units come
+//     largest first; the last few (a problem's ntail) run as 256-column
+//     items with two blocks per wave, so the final round of workgroups is
+//     made of half-length pieces.
 //   * Each group's scale and bias are read once per work unit with coalesced
 //     loads into an LDS table of fp16 (s, b + 8s) pairs.
 //   * Weights go HBM -> VGPR with one 128-bit load per lane and column block
@@ -59,19 +62,20 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kGemmThreads / 64;
-constexpr int kCols = 512;                        // weight rows (output columns) per workgroup
-constexpr int kCB = kCols / (16 * kWaves);        // 16-column MFMA blocks per wave
-constexpr int kHalf = kCB / 2;                    // gate blocks (then as many up blocks) in SwiGLU mode
+constexpr int kColsMax = 512;                     // weight rows (output columns) of a full-width item
+constexpr int kCBFull = kColsMax / (16 * kWaves); // 16-column MFMA blocks per wave, full-width items
+
 constexpr int kKStep = 128;                       // K per step (4 quarters x 32)
 constexpr int kRowBytes = kKStep * 2;             // one row of one step in LDS (fp16)
 constexpr int kBufBytes = kUnitRows * kRowBytes;  // one step of a full unit (24 KiB)
 constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 
 constexpr int kTabGroups = 32;                     // scale/bias groups held at a time (2048 inputs)
-constexpr int kTabStride = kCols + 16;             // dwords per group row of the table (padded)
+constexpr int kTabStride = kColsMax + 16;          // dwords per group row of the table (padded)
 
+template <int CB>
 struct BStage {
-  u4 q[kCB];           // 4 code words (32 codes) per column block
+  u4 q[CB];            // 4 code words (32 codes) per column block
 };
 
 __device__ __forceinline__ uint32_t pack_scale_bias(uint32_t s_bits, uint32_t b_bits) {
@@ -113,10 +117,13 @@ struct Unit {
 
 // NRB = 16-row MFMA blocks of the unit (1..6), fixed at compile time so a K
 // step is one branch-free block the compiler can schedule as a whole.
-template <int MODE, bool AF16, int NRB>
+template <int MODE, bool AF16, int NRB, int CB>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
   constexpr int kMaxRB = NRB;
+  constexpr int kCB = CB;                    // 16-column MFMA blocks per wave
+  constexpr int kHalf = CB / 2;              // gate blocks (then as many up blocks) in SwiGLU mode
+  constexpr int kCols = 16 * CB * kWaves;    // weight rows (output columns) of this item
   constexpr int kRB32 = (NRB + 1) / 2;                                    // 32-row blocks staged
   constexpr int kSlabs = (32 * kRB32 / kSlabRows + kWaves - 1) / kWaves;  // A stores per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -174,7 +181,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // first input of this lane's quarter at step s (valid iff < K)
   auto lane_k0 = [&](int s) { return kKStep * s + 32 * kq; };
 
-  auto load_b = [&](BStage &st, int s) {
+  auto load_b = [&](BStage<kCB> &st, int s) {
     const int k0 = lane_k0(s);
     const int kc = k0 < K ? k0 : 0;
 #pragma unroll
@@ -294,7 +301,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint32_t m_lo = vgpr_const(0x000F000Fu), m_hi = vgpr_const(0x00F000F0u);
   const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
 
-  auto compute = [&](const BStage &st, int s, int buf) {
+  auto compute = [&](const BStage<kCB> &st, int s, int buf) {
     const int k0 = lane_k0(s);
     const bool kvalid = k0 < K;
     const int gt = ((k0 >> 6) & (kTabGroups - 1)) * kTabStride;  // group row in the table
@@ -361,7 +368,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // requested, step s is computed, then A(s+1) is written to LDS. Loads are
   // issued unconditionally (clamped to the last step) so every step has the
   // same number in flight and the compiler's wait counts stay exact.
-  auto body = [&](int s, const BStage &cur, BStage &nxt) {
+  auto body = [&](int s, const BStage<kCB> &cur, BStage<kCB> &nxt) {
     lds_barrier();
     if (s > 0 && s < steps && (s & 15) == 0) {  // next 2048 inputs: next table chunk
       fill_table(s >> 4);
@@ -374,7 +381,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     store_a((s + 1) & 1);
   };
 
-  BStage b0, b1;
+  BStage<kCB> b0, b1;
   fill_table(0);
   load_a(0);
   load_b(b0, 0);
@@ -442,17 +449,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   // units (one per XCD); the N-slices of one unit stay on one XCD, so its
   // gathered activation rows are fetched into that XCD's L2 once.
   const int lb = b - P.wg_begin;
-  const int slot = lb >> 3;
   Unit U;
-  const int unit = (slot / P.nslices) * 8 + (lb & 7);
-  U.slice = slot % P.nslices;
+  int unit, nsl = P.nslices;
+  bool narrow = false;
   if (P.units) {
-    if (unit >= *P.num_units) return;
+    // Listed units (largest first): all but the last ntail or so run as
+    // nslices full-width items; the tail runs as 2 * nslices half-width
+    // items, so the last round is made of short pieces. nbig is a multiple
+    // of 8, so both parts keep a unit's slices on one XCD.
+    const int nu = *P.num_units;
+    const int nbig = P.ntail > 0 ? max(nu - P.ntail, 0) & ~7 : nu;
+    const int big_wgs = ((nbig + 7) & ~7) * nsl;  // whole groups of 8 units
+    int j = lb;
+    if (j >= big_wgs) {
+      j -= big_wgs;
+      nsl *= 2;
+      narrow = true;
+    }
+    const int slot = j >> 3;
+    unit = (narrow ? nbig : 0) + (slot / nsl) * 8 + (j & 7);
+    U.slice = slot % nsl;
+    if (unit >= nu) return;
     const int32_t *u = P.units + 3 * (int64_t)unit;
     U.e = u[0];
     U.r0 = u[1];
     U.nr = min(u[2], kUnitRows);
   } else {
+    const int slot = lb >> 3;
+    unit = (slot / nsl) * 8 + (lb & 7);
+    U.slice = slot % nsl;
     U.e = 0;
     U.r0 = unit * kUnitRows;
     U.nr = min(kUnitRows, P.implicit_rows - U.r0);
@@ -465,13 +490,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   }
   __syncthreads();
 
-  switch ((U.nr + 15) >> 4) {
-    case 1: run_unit<MODE, AF16, 1>(P, U, lds, s_arow, tab); break;
-    case 2: run_unit<MODE, AF16, 2>(P, U, lds, s_arow, tab); break;
-    case 3: run_unit<MODE, AF16, 3>(P, U, lds, s_arow, tab); break;
-    case 4: run_unit<MODE, AF16, 4>(P, U, lds, s_arow, tab); break;
-    case 5: run_unit<MODE, AF16, 5>(P, U, lds, s_arow, tab); break;
-    default: run_unit<MODE, AF16, 6>(P, U, lds, s_arow, tab); break;
+  // half-width items: the same code with half the column blocks per wave
+  if (narrow) {
+    switch ((U.nr + 15) >> 4) {
+      case 1: run_unit<MODE, AF16, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+    }
+  } else {
+    switch ((U.nr + 15) >> 4) {
+      case 1: run_unit<MODE, AF16, 1, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, 2, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, 3, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, 4, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, 5, kCBFull>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, 6, kCBFull>(P, U, lds, s_arow, tab); break;
+    }
   }
 }
 

@@ -19,6 +19,9 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;
 constexpr int kMaxTopK = 64;  // one selected expert per lane of the top-k wave
+// Trailing units of the gate/up work list that run as half-width items, so
+// the last round of workgroups is made of short pieces.
+constexpr int kNarrowTail = 32;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -234,9 +237,11 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.N = 2 * f; p.K = d;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(f, 256);
+    p.ntail = kNarrowTail;
     p.wg_begin = nwg;
     p.H = w.h; p.ldh = f;
-    nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
+    // full-width items, plus up to ntail + 14 units' extra half-width items
+    nwg += problem_wgs(max_units_routed(T, k, E) + 2 * (kNarrowTail + 16), p.nslices);
   }
   g1.nprob = np;
   g1.total_wg = nwg;

@@ -82,6 +82,7 @@ struct GemmProblem {
   const int32_t *num_units;  // device count of units
   int implicit_rows;         // implicit units: rows [0, implicit_rows) of expert 0
   int nslices;               // workgroups per unit along N
+  int ntail;                 // listed units: about this many trailing units run as 2*nslices half-width items
   int wg_begin;              // first workgroup (in remapped order) of this problem
   // outputs
   float *C; int ldc;          // kStoreC

@@ -90,11 +90,17 @@ __device__ __forceinline__ void topk_wave(const float *row, int E, int k, int la
   my_id = 0;
   for (int j = 0; j < k; ++j) {
     // wave maximum of the heads: first over the logit half of the key, then
-    // over the index half among the lanes that hold that logit
+    // (only when several lanes hold that logit) over the index half among them
     const uint32_t hi = (uint32_t)(key[0] >> 32);
     const uint32_t mhi = wave_max32(hi);
-    const uint32_t lo = hi == mhi ? (uint32_t)key[0] : 0u;
-    const uint64_t win = ((uint64_t)mhi << 32) | wave_max32(lo);
+    const uint64_t holders = __ballot(hi == mhi);
+    uint64_t win;
+    if (__popcll(holders) == 1) {  // one lane holds the maximum logit: its head wins
+      win = readlane64(key[0], __ffsll((long long)holders) - 1);
+    } else {
+      const uint32_t lo = hi == mhi ? (uint32_t)key[0] : 0u;
+      win = ((uint64_t)mhi << 32) | wave_max32(lo);
+    }
     if (key[0] == win) {  // keys are distinct: one lane wins and drops its head
 #pragma unroll
       for (int r = 0; r + 1 < VPL; ++r) key[r] = key[r + 1];
