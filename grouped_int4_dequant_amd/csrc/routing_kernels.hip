@@ -17,13 +17,13 @@
 //         same workgroups then convert x to fp16 for the GEMMs.
 //   count one workgroup per 64-token sub-chunk c: per-expert counts of its
 //         pairs, cnt[c][e].
-//   scan  one workgroup per sub-chunk: column sums of cnt give the expert
+//   scatter one workgroup per sub-chunk: column sums of cnt give the expert
 //         totals and the counts before its sub-chunk, an exclusive scan over
 //         experts gives the offsets, and a 64-bit token mask per expert for
 //         its own sub-chunk gives the stable scatter:
 //           pos = offset[e] + before[e] + popcount(mask[e] & tokens below t).
 //         Integer atomics commute, so the result is deterministic.
-//         Workgroup 0 also writes counts, offsets, the 32-row block map and
+//         One more workgroup writes counts, offsets, the 32-row block map and
 //         the GEMM work list.
 //
 // Pages cited (titles as published):
@@ -70,20 +70,41 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x % kWave;
   const int gwave = blockIdx.x * kWaves + threadIdx.x / kWave;
   const int nwaves = gridDim.x * kWaves;
-  for (int t = gwave; t < a.T; t += nwaves) route_token<VPL>(a, t, lane);
-  if (a.x16 == nullptr) return;
-
-  // x (bf16, natural order) -> x16 (fp16, each 8-run stored as 0,4,1,5,2,6,3,7)
+  // x (bf16, natural order) -> x16 (fp16, each 8-run stored as 0,4,1,5,2,6,3,7).
+  // The first kUnroll 16-byte chunks of this thread are requested before the
+  // top-k, so their latency hides behind it.
+  constexpr int kUnroll = 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t n8 = (int64_t)a.T * a.d / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
-    const uint4 v = reinterpret_cast<const uint4 *>(a.x)[i];
-    // v.x = (e0,e1) v.y = (e2,e3) v.z = (e4,e5) v.w = (e6,e7)
-    const uint32_t p0 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));  // (e0,e4)
-    const uint32_t p1 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u));  // (e1,e5)
-    const uint32_t p2 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));  // (e2,e6)
-    const uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u));  // (e3,e7)
-    reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
+  const int64_t n8 = a.x16 ? (int64_t)a.T * a.d / 8 : 0;
+  int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint4 v[kUnroll];
+  auto load = [&]() {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      v[u] = i < n8 ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load();
+  for (int t = gwave; t < a.T; t += nwaves) route_token<VPL>(a, t, lane);
+  for (; i0 < n8; i0 += kUnroll * stride) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n8) {
+        // v.x = (e0,e1) v.y = (e2,e3) v.z = (e4,e5) v.w = (e6,e7)
+        const uint32_t p0 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].z, v[u].x, 0x05040100u));  // (e0,e4)
+        const uint32_t p1 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].z, v[u].x, 0x07060302u));  // (e1,e5)
+        const uint32_t p2 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].w, v[u].y, 0x05040100u));  // (e2,e6)
+        const uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].w, v[u].y, 0x07060302u));  // (e3,e7)
+        reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
+      }
+    }
+    if (i0 + kUnroll * stride < n8) {
+      i0 += kUnroll * stride;
+      load();
+      i0 -= kUnroll * stride;
+    }
   }
 }
 
@@ -172,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void count_kernel(ScanArgs a) {
 // (column sums of cnt), offsets by an exclusive scan over experts, and the
 // stable scatter of c's pairs:
 //   pos = offset[e] + before[e] + popcount(mask[e] & tokens of c below t).
-// Workgroup 0 also writes counts, offsets, the 32-row block map and the GEMM
-// work list.
+// One extra workgroup (the last, with no pairs of its own) writes counts,
+// offsets, the 32-row block map and the GEMM work list meanwhile.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
@@ -182,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ int s_scratch[kWaves];
   const int E = a.E, k = a.k, T = a.T;
-  const int c = blockIdx.x, C = gridDim.x;
+  const int c = blockIdx.x, C = gridDim.x - 1;  // sub-chunks; workgroup C holds none
   const int64_t tk = (int64_t)T * k;
   const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
 
@@ -220,9 +241,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
     a.sorted_token[pos] = t;
     a.pair_pos[idx] = pos;
   }
-  if (c != 0) return;
+  if (c != C) return;
 
-  // workgroup 0: counts, offsets, block map and GEMM work list
+  // the last workgroup (which holds no pairs): counts, offsets, block map and
+  // GEMM work list, beside the scatter of the others
   for (int e = threadIdx.x; e < E; e += kThreads) {
     a.counts[e] = s_tot[e];
     a.offsets[e] = s_off[e];
@@ -313,7 +335,8 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s, hipEvent_t stop) {
   hipLaunchKernelGGL(count_kernel, dim3(C), dim3(kThreads), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipExtLaunchKernelGGL(scatter_kernel, dim3(C), dim3(kThreads), 0, s, nullptr, stop, 0, a);
+  // one workgroup per sub-chunk, plus one for the block map and work list
+  hipExtLaunchKernelGGL(scatter_kernel, dim3(C + 1), dim3(kThreads), 0, s, nullptr, stop, 0, a);
   return hipGetLastError();
 }
 
