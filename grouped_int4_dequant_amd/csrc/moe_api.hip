@@ -19,7 +19,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;
 constexpr int kMaxTopK = 64;  // one selected expert per lane of the top-k wave
-// Trailing units of the gate/up work list that run as half-width items, so
+// Trailing units of the routed work lists that run as half-width items, so
 // the last round of workgroups is made of short pieces.
 constexpr int kNarrowTail = 32;
 
@@ -272,9 +272,10 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.N = d; p.K = f;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(d, 512);
+    p.ntail = kNarrowTail;
     p.wg_begin = nwg;
     p.H = w.o; p.ldh = d;
-    nwg += problem_wgs(max_units_routed(T, k, E), p.nslices);
+    nwg += problem_wgs(max_units_routed(T, k, E) + 2 * (kNarrowTail + 16), p.nslices);
   }
   g2.nprob = np;
   g2.total_wg = nwg;
