@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB three times "
                          "(a known-size kernel for calibrating hardware byte counters; 0: none)")
+    ap.add_argument("--ablations", type=str, default="",
+                    help="comma-separated token counts: also time the layer's ablation forms "
+                         "(16-row work units; routing built on the host) at each (e.g. 512,2048)")
     return ap.parse_args()
 
 
@@ -224,11 +227,43 @@ def main():
 
     if args.decode_steps > 0:
         out["decode_t1"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events)
+    if args.ablations:
+        out["ablations_us"] = bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream,
+                                              [int(t) for t in args.ablations.split(",")],
+                                              args.steps, args.warmup)
     del layer, x, lg, y, ws
     torch.cuda.empty_cache()
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream, tokens, steps, warmup):
+    """Wall-clock microseconds per call of each ablation form over the first T
+    tokens of the benchmark input, calls back to back on one stream."""
+    res = {}
+    for T in tokens:
+        if not 0 < T <= x.shape[0]:
+            raise ValueError(f"ablation token count {T} outside 1..{x.shape[0]}")
+        row = {}
+        for name, variant in moe.ABLATIONS.items():
+            args = (B.ctypes.byref(layer.c), x.data_ptr(), lg.data_ptr(), T, y.data_ptr(), None,
+                    ws.data_ptr(), ws.numel(), stream.cuda_stream, variant)
+
+            def call():
+                st = lib.moe_layer_forward_ablation(*args)
+                if st != 0:
+                    raise RuntimeError(moe.status_string(st))
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            row[name] = (time.perf_counter() - t0) * 1e6 / steps
+        res[str(T)] = row
+    return res
 
 
 def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):

@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
         lib.moe_layer_forward.restype = ctypes.c_int
         lib.moe_prefill_chunked.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _I32, _P, _P,
                                             ctypes.c_size_t, _P]
+        lib.moe_layer_forward_ablation.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
+                                                   ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P,
+                                                   _I32]
+        lib.moe_layer_forward_ablation.restype = ctypes.c_int
         lib.moe_prefill_chunked.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
@@ -231,6 +235,29 @@ def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
                                     y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
                                     ws.data_ptr(), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2}
+
+
+def layer_forward_ablation(layer: Layer, x: torch.Tensor, logits: torch.Tensor, variant: str,
+                           y: Optional[torch.Tensor] = None,
+                           routing: Optional[Dict[str, torch.Tensor]] = None,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_layer_forward_ablation: the prefill sequence with one of the pages'
+    ablations ("none", "tile16", "host_routing"); measurement only."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(logits, "logits", torch.float32, (T, layer.E))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load().moe_layer_forward_ablation(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                             y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
+                                             ws.data_ptr(), ws.numel(), _stream(stream), ABLATIONS[variant]),
+           "moe_layer_forward_ablation")
     return y
 
 

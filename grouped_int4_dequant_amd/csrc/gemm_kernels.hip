@@ -478,9 +478,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
     const int slot = lb >> 3;
     unit = (slot / nsl) * 8 + (lb & 7);
     U.slice = slot % nsl;
+    const int urows = P.unit_rows > 0 ? P.unit_rows : kUnitRows;
     U.e = 0;
-    U.r0 = unit * kUnitRows;
-    U.nr = min(kUnitRows, P.implicit_rows - U.r0);
+    U.r0 = unit * urows;
+    U.nr = min(urows, P.implicit_rows - U.r0);
     if (U.nr <= 0) return;
   }
 

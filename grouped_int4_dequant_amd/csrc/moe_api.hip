@@ -11,6 +11,7 @@
 #include "moe_internal.h"
 
 #include <algorithm>
+#include <vector>
 
 using namespace moe;
 
@@ -39,7 +40,20 @@ struct Carver {
   }
 };
 
-int64_t max_units_routed(int T, int k, int E) { return ceil_div((int64_t)T * k, kUnitRows) + E; }
+constexpr int kMinUnitRows = 16;  // smallest work unit (the 16-row tile variant)
+
+int64_t max_units_routed(int T, int k, int E, int unit_rows = kUnitRows) {
+  return ceil_div((int64_t)T * k, unit_rows) + E;
+}
+
+// Layer forward variants: the default, and the pages' ablations (measurement
+// only, through moe_layer_forward_ablation).
+struct FwdOptions {
+  int unit_rows = kUnitRows;  // rows per GEMM work unit at most
+  int ntail = 0;              // routed units run as half-width items at the end
+  bool host_routing = false;  // counts, offsets, scatter, block map and work list built on the host
+  bool few_token_form = true; // calls of at most 8 tokens take the two-kernel decode form
+};
 
 int check_layer(const moe_layer_t *L) {
   if (!L) return MOE_EINVAL;
@@ -91,7 +105,7 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.rt.pair_pos = c.take<int32_t>(tk);
   o.rt.block_map = c.take<int32_t>(3 * (size_t)moe_max_blocks(T, E, k));
   o.rt.num_blocks = c.take<int32_t>(1);
-  o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E));
+  o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E, kMinUnitRows));  // any unit size
   o.num_units = c.take<int32_t>(1);
   o.chunk_counts = c.take<int32_t>((size_t)ceil_div(T, kSubChunk) * E);
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
@@ -114,7 +128,7 @@ int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
                   int32_t *chunk_counts, int32_t *units, int32_t *num_units, const uint16_t *x,
-                  uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr) {
+                  uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr, int unit_rows = kUnitRows) {
   TopkArgs ta{};
   ta.logits = logits;
   ta.T = T;
@@ -144,7 +158,8 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   sa.units = units;
   sa.chunk_counts = chunk_counts;
   sa.num_units = num_units;
-  sa.max_units = units ? (int)max_units_routed(T, k, E) : 0;
+  sa.max_units = units ? (int)max_units_routed(T, k, E, unit_rows) : 0;
+  sa.unit_rows = unit_rows;
   return hip_status(launch_scan(sa, s, ev ? ev[2] : nullptr));
 }
 
@@ -170,9 +185,77 @@ int enqueue_combine(int T, int d, int k, const uint16_t *o, const uint16_t *o_sh
   return hip_status(launch_combine(ca, s, ev ? ev[4] : nullptr));
 }
 
+// The pages' "before" configuration: after the top-k kernel, the selected
+// expert ids come back to the host, which builds counts, offsets, the stable
+// scatter, the 32-row block map and the GEMM work list (the same results as
+// the scan/scatter kernels), and sends them back. Synchronises the stream
+// twice. Measurement only.
+int host_route(int T, int E, int k, int unit_rows, const moe_routing_t &rt, int32_t *units,
+               int32_t *num_units, hipStream_t s) {
+  const int64_t tk = (int64_t)T * k;
+  std::vector<int32_t> ids(tk);
+  if (hipMemcpyAsync(ids.data(), rt.topk_ids, tk * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_EHIP;
+  std::vector<int32_t> cnt(E, 0), off(E + 1, 0), cur(E, 0), sorted_pair(tk), sorted_token(tk), pair_pos(tk);
+  for (int64_t i = 0; i < tk; ++i) ++cnt[ids[i]];
+  for (int e = 0; e < E; ++e) off[e + 1] = off[e] + cnt[e];
+  for (int64_t i = 0; i < tk; ++i) {  // ascending pair index: stable
+    const int e = ids[i];
+    const int pos = off[e] + cur[e]++;
+    sorted_pair[pos] = (int32_t)i;
+    sorted_token[pos] = (int32_t)(i / k);
+    pair_pos[i] = pos;
+  }
+  const int max_blocks = moe_max_blocks(T, E, k);
+  std::vector<int32_t> bmap(3 * (size_t)max_blocks);
+  int nb = 0;
+  for (int e = 0; e < E; ++e)
+    for (int b = 0; b * MOE_BLOCK_ROWS < cnt[e]; ++b, ++nb) {
+      bmap[3 * nb] = e;
+      bmap[3 * nb + 1] = off[e] + b * MOE_BLOCK_ROWS;
+      bmap[3 * nb + 2] = std::min(MOE_BLOCK_ROWS, cnt[e] - b * MOE_BLOCK_ROWS);
+    }
+  for (int i = nb; i < max_blocks; ++i) {
+    bmap[3 * i] = -1;
+    bmap[3 * i + 1] = 0;
+    bmap[3 * i + 2] = 0;
+  }
+  // work list: the same units as the scatter kernel, largest size class first
+  std::vector<int32_t> ulist;
+  const int classes = kUnitRows / 16;
+  for (int c = classes; c >= 1; --c)
+    for (int e = 0; e < E; ++e) {
+      const int tot = cnt[e], nu = (tot + unit_rows - 1) / unit_rows;
+      for (int u = 0; u < nu; ++u) {
+        const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
+        if ((b1 - b0 + 15) / 16 != c) continue;
+        ulist.push_back(e);
+        ulist.push_back(off[e] + b0);
+        ulist.push_back(b1 - b0);
+      }
+    }
+  const int32_t nunits = (int32_t)(ulist.size() / 3);
+  struct Copy { void *dst; const void *src; size_t bytes; };
+  const Copy copies[] = {
+      {rt.counts, cnt.data(), E * sizeof(int32_t)},
+      {rt.offsets, off.data(), (E + 1) * sizeof(int32_t)},
+      {rt.sorted_pair, sorted_pair.data(), tk * sizeof(int32_t)},
+      {rt.sorted_token, sorted_token.data(), tk * sizeof(int32_t)},
+      {rt.pair_pos, pair_pos.data(), tk * sizeof(int32_t)},
+      {rt.block_map, bmap.data(), bmap.size() * sizeof(int32_t)},
+      {rt.num_blocks, &nb, sizeof(int32_t)},
+      {units, ulist.data(), ulist.size() * sizeof(int32_t)},
+      {num_units, &nunits, sizeof(int32_t)},
+  };
+  for (const Copy &c : copies)
+    if (c.bytes && hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyHostToDevice, s) != hipSuccess) return MOE_EHIP;
+  return hip_status(hipStreamSynchronize(s));  // the host vectors must outlive the copies
+}
+
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
-                hipEvent_t *ev = nullptr) {
+                hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true}) {
   const size_t need = carve_layer(T, L, nullptr, nullptr);
   if (ws_bytes < need) return MOE_EWORKSPACE;
   Workspace w;
@@ -187,7 +270,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     return MOE_EUNSUPPORTED;
 
   int st = MOE_OK;
-  if (decode_supported(T, L)) {
+  if (opt.few_token_form && decode_supported(T, L)) {
     // A few tokens: gate/up (routing repeated inside) and down + combine.
     // Routing tensors are produced by the routing kernels only when asked for.
     if (routing) {
@@ -211,7 +294,16 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     return hip_status(launch_decode(a, s, gu_start, ev ? ev[3] : nullptr, ev ? ev[4] : nullptr));
   }
 
-  st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev);
+  if (opt.host_routing) {
+    TopkArgs ta{};
+    ta.logits = logits; ta.T = T; ta.E = E; ta.k = k;
+    ta.topk_ids = rt.topk_ids; ta.topk_w = rt.topk_w;
+    ta.x = x; ta.x16 = w.x16; ta.d = d;
+    st = hip_status(launch_topk(ta, s));
+    if (st == MOE_OK) st = host_route(T, E, k, opt.unit_rows, rt, w.units, w.num_units, s);
+  } else {
+    st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev, opt.unit_rows);
+  }
   if (st != MOE_OK) return st;
 
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
@@ -223,11 +315,11 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->sh_gu_q; p.Ws = L->sh_gu_s; p.Wb = L->sh_gu_b;
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = 2 * fs; p.K = d;
-    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
+    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(fs, 256);
     p.wg_begin = nwg;
     p.H = w.h_sh; p.ldh = fs;
-    nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
+    nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
   }
   {
     GemmProblem &p = g1.prob[np++];
@@ -237,11 +329,11 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.N = 2 * f; p.K = d;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(f, 256);
-    p.ntail = kNarrowTail;
+    p.ntail = opt.ntail;
     p.wg_begin = nwg;
     p.H = w.h; p.ldh = f;
     // full-width items, plus up to ntail + 14 units' extra half-width items
-    nwg += problem_wgs(max_units_routed(T, k, E) + 2 * (kNarrowTail + 16), p.nslices);
+    nwg += problem_wgs(max_units_routed(T, k, E, opt.unit_rows) + 2 * (opt.ntail + 16), p.nslices);
   }
   g1.nprob = np;
   g1.total_wg = nwg;
@@ -258,11 +350,11 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->sh_dn_q; p.Ws = L->sh_dn_s; p.Wb = L->sh_dn_b;
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = d; p.K = fs;
-    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T;
+    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(d, 512);
     p.wg_begin = nwg;
     p.H = w.o_sh; p.ldh = d;
-    nwg += problem_wgs(ceil_div(T, kUnitRows), p.nslices);
+    nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
   }
   {
     GemmProblem &p = g2.prob[np++];
@@ -272,10 +364,10 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.N = d; p.K = f;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(d, 512);
-    p.ntail = kNarrowTail;
+    p.ntail = opt.ntail;
     p.wg_begin = nwg;
     p.H = w.o; p.ldh = d;
-    nwg += problem_wgs(max_units_routed(T, k, E) + 2 * (kNarrowTail + 16), p.nslices);
+    nwg += problem_wgs(max_units_routed(T, k, E, opt.unit_rows) + 2 * (opt.ntail + 16), p.nslices);
   }
   g2.nprob = np;
   g2.total_wg = nwg;
@@ -373,6 +465,27 @@ int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float
   if (!x || !logits || !y || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
   return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream, events);
+}
+
+int moe_layer_forward_ablation(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                               float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                               hipStream_t stream, int32_t variant) {
+  FwdOptions opt{kUnitRows, kNarrowTail, false, false};
+  switch (variant) {
+    case MOE_ABLATION_NONE: break;
+    case MOE_ABLATION_TILE16: opt.unit_rows = 16; opt.ntail = 0; break;
+    case MOE_ABLATION_HOST_ROUTING: opt.host_routing = true; break;
+    default: return MOE_EINVAL;
+  }
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream, nullptr, opt);
 }
 
 int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,

@@ -50,6 +50,7 @@ struct ScanArgs {
   int max_blocks;
   int32_t *units, *num_units;   // optional GEMM work list (nullptr: none)
   int max_units;
+  int unit_rows;                // rows per GEMM work unit at most (16..kUnitRows)
   int32_t *chunk_counts;        // scratch [ceil(T/64)][E]
 };
 
@@ -81,6 +82,7 @@ struct GemmProblem {
   const int32_t *units;      // [*][3] (expert, first row, rows <= 128); nullptr: implicit
   const int32_t *num_units;  // device count of units
   int implicit_rows;         // implicit units: rows [0, implicit_rows) of expert 0
+  int unit_rows;             // implicit units: rows per unit (16..kUnitRows; 0 means kUnitRows)
   int nslices;               // workgroups per unit along N
   int ntail;                 // listed units: about this many trailing units run as 2*nslices half-width items
   int wg_begin;              // first workgroup (in remapped order) of this problem

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   if (threadIdx.x == 0) *a.num_blocks = nblocks;
   if (a.units == nullptr) return;
   __syncthreads();
-  // Work list: each expert's rows split evenly into ceil(rows / kUnitRows)
+  // Work list: each expert's rows split evenly into ceil(rows / unit_rows)
   // units, listed by 16-row size class, largest first, so the GEMM (which
   // hands units to workgroups in list order) starts the longest ones first.
   // The order within a class follows LDS atomics; it changes which
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   if (threadIdx.x <= kClasses) s_cls[threadIdx.x] = 0;
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + kUnitRows - 1) / kUnitRows;
+    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
     for (int u = 0; u < nu; ++u) {
       const int rows = (int)((int64_t)(u + 1) * tot / nu) - (int)((int64_t)u * tot / nu);
       atomicAdd(&s_cls[kClasses - (rows + 15) / 16], 1);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + kUnitRows - 1) / kUnitRows;
+    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
     for (int u = 0; u < nu; ++u) {
       const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
       const int slot = atomicAdd(&s_cls[kClasses - (b1 - b0 + 15) / 16], 1);

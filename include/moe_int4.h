@@ -215,6 +215,29 @@ int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float
                             void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *events);
 
 /*
+ * The layer with one of the pages' ablations, for measurement only (Lily-EN
+ * "Prefill: Keep Weights Packed, Keep Routing on the GPU" and Lily-ES
+ * "Precarga...": routing kept on the GPU and 32-row rather than 16-row
+ * tiles are two of the changes they measure). Always takes the prefill form
+ * (also for T <= 8); otherwise as moe_layer_forward, with the same results.
+ *   MOE_ABLATION_NONE          the default prefill sequence
+ *   MOE_ABLATION_TILE16        GEMM work units of at most 16 rows (instead of
+ *                              96), so each rebuilt weight feeds 16 rows
+ *   MOE_ABLATION_HOST_ROUTING  after the top-k kernel, the expert ids are
+ *                              copied to the host, which builds counts,
+ *                              offsets, scatter, block map and work list and
+ *                              copies them back: synchronises the stream
+ *                              twice and allocates host memory
+ * Errors: as moe_layer_forward; MOE_EINVAL for an unknown variant.
+ */
+#define MOE_ABLATION_NONE 0
+#define MOE_ABLATION_TILE16 1
+#define MOE_ABLATION_HOST_ROUTING 2
+int moe_layer_forward_ablation(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                               float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                               hipStream_t stream, int32_t variant);
+
+/*
  * Bounded-chunk prefill for long prompts (Lily-ES "Precarga...", Lily-HE
  * prefill section: long prompts run in bounded chunks so temporary
  * activations do not compete with weights for memory). Runs

@@ -90,6 +90,18 @@ def test_layer_forward_rejects_bad_buffers():
     assert fwd(0x1000, 0x1000, 1 << 22, 0x1000, None, 0x1000, 1 << 40, None) == B.MOE_EUNSUPPORTED
 
 
+def test_ablation_entry_point_validates_like_the_forward():
+    L = qwen_layer_struct()
+    lib = moe.load()
+    abl = lambda *a: lib.moe_layer_forward_ablation(ctypes.byref(L), *a)
+    for v in moe.ABLATIONS.values():
+        assert abl(0x1000, 0x1000, 0, 0x1000, None, 0x1000, 0, None, v) == B.MOE_OK
+        assert abl(None, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, v) == B.MOE_EINVAL
+        assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 100, None, v) == B.MOE_EWORKSPACE
+    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, 3) == B.MOE_EINVAL
+    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, -1) == B.MOE_EINVAL
+
+
 def test_route_and_gemm_reject_bad_arguments():
     lib = moe.load()
     r = B.MoeRoutingT(*([0x1000] * 9))

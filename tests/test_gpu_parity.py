@@ -303,6 +303,50 @@ def test_decode_tied_logits(moe):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, 8), "decode ties")
 
 
+# ------------------------------------------------------------------ ablations
+ABLATION_SHAPES = [
+    # T, d, f, E, k, f_sh
+    (64, 256, 128, 16, 2, 128),
+    (1, 256, 128, 16, 2, 128),      # one token through the prefill form
+    (129, 320, 192, 8, 8, 64),
+    (256, 1024, 256, 64, 4, 256),
+    (250, 1024, 512, 3, 2, 0),      # streaming GEMM, experts over several units
+    (130, 1536, 1024, 6, 2, 1024),
+]
+
+
+@pytest.mark.parametrize("variant", ["tile16", "host_routing"])
+@pytest.mark.parametrize("T,d,f,E,k,f_sh", ABLATION_SHAPES)
+def test_ablation_matches_oracle(moe, variant, T, d, f, E, k, f_sh):
+    """The ablation forms (16-row work units; routing built on the host) compute
+    the same layer: routing exact, outputs to the same tolerance."""
+    p = S.make_custom(T, S.LayerShape(d=d, f=f, E=E, k=k, f_sh=f_sh), seed=T + d + f + E)
+    say(f"ablation {variant} T={T} d={d} f={f} E={E} k={k} f_sh={f_sh}")
+    layer, x, lg = upload(p, moe)
+    routing = moe.alloc_routing(T, E, k)
+    y = moe.layer_forward_ablation(layer, x, lg, variant, routing=routing)
+    y_def = moe.layer_forward(layer, x, lg)
+    torch.cuda.synchronize()
+    check_routing(routing, O.route(p.logits, k), T, k)
+    y = y.cpu().numpy()
+    say(f"  max |ablation - default| = {np.max(np.abs(y - y_def.cpu().numpy())):.3e}")
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"{variant} {T},{d},{f},{E},{k},{f_sh}")
+
+
+@pytest.mark.parametrize("variant", ["tile16", "host_routing"])
+def test_ablation_full_config(moe, variant):
+    p = S.make_problem(1)
+    say(f"ablation {variant} config 1 T={p.T} (routing full, outputs sampled)")
+    layer, x, lg = upload(p, moe)
+    routing = moe.alloc_routing(p.T, p.shape.E, p.shape.k)
+    y = moe.layer_forward_ablation(layer, x, lg, variant, routing=routing)
+    torch.cuda.synchronize()
+    check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
+    tok = _sample(p.T, seed=11)
+    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+    check_output(y.cpu().numpy()[tok], y_ref, f"{variant} config 1 sampled")
+
+
 def test_zero_tokens_is_a_noop(moe):
     p = S.make_problem(0)
     layer, x, lg = upload(p, moe)
