@@ -55,7 +55,8 @@ __device__ __forceinline__ uint32_t group_consts(const u4v &sw, const u4v &bw, i
   return rb_pack_scale_bias((sw[s] >> sh) & 0xFFFFu, (bw[s] >> sh) & 0xFFFFu);
 }
 
-template <int VPL>
+// ONE: calls of one token (T == 1), whose k picks are the distinct experts.
+template <int VPL, bool ONE>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a) {
   __shared__ int s_ids[kDecodeMaxPairs];
   __shared__ uint32_t s_bits[MOE_MAX_EXPERTS / 32];
@@ -72,8 +73,37 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   const int u = blockIdx.x / chunks, hc = blockIdx.x - u * chunks;
   const bool shared = u == P;
 
+  // ---- the call's activations (bf16 [T][d]) are requested first, for LDS;
+  // their latency hides behind the routing
+  extern __shared__ uint4 s_x[];  // [T * d / 8]
+  // T * d / 8 chunks over 64 * d / 512 threads: T chunks per thread, all
+  // requested unconditionally (past T: the last chunk again), so none waits
+  // on another
+  constexpr int kXPer = ONE ? 1 : kDecodeMaxT;
+  uint4 xr_[kXPer];
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) xr_[i] = reinterpret_cast<const uint4 *>(a.x)[tid + min(i, T - 1) * nthreads];
+
   // ---- routing, repeated by every workgroup of a routed expert
-  if (!shared) {
+  if (!shared && ONE) {
+    // one token: its k picks are the distinct experts, in slot order
+    if (wave == 0) {
+      int id;
+      float g;
+      topk_wave<VPL>(a.logits, E, k, lane, id, g);
+      if (lane < k) {
+        s_ids[lane] = id;
+        s_uexp[lane] = id;
+        s_umask[lane] = 1u;
+        if (blockIdx.x == 0) {
+          a.ids[lane] = id;
+          a.gates[lane] = g;
+        }
+      }
+      if (lane == 0) s_U = k;
+    }
+    __syncthreads();
+  } else if (!shared) {
   for (int i = tid; i < nwords; i += nthreads) s_bits[i] = 0u;
   if (tid < kDecodeMaxPairs) s_umask[tid] = 0u;
   if (wave == 0) {
@@ -143,15 +173,23 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     sw[cb] = *reinterpret_cast<const u4v *>(wsc + (int64_t)row[cb] * G + kbase / 64);
     bw[cb] = *reinterpret_cast<const u4v *>(wbi + (int64_t)row[cb] * G + kbase / 64);
   }
+  // activations into LDS (their loads were issued first), then row c16's
+  // fragments (a token of the mask, else the first token's, zeroed at use)
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i)
+    if (i < T) s_x[tid + i * nthreads] = xr_[i];  // LDS stores only: no load depends on them
+  __syncthreads();
   const bool has_row = c16 < nrows;
-  const int tok = has_row ? nth_bit(mask, c16) : 0;
-  const uint16_t *xr = a.x + (int64_t)tok * d + kbase + 32 * kq;
+  const int tok = nth_bit(mask, has_row ? c16 : 0);
+  const uint4 *xl = s_x + ((int64_t)tok * d + kbase + 32 * kq) / 8;
   u4v xv[kSteps][4];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xv[s][j] = has_row ? *reinterpret_cast<const u4v *>(xr + 128 * s + 8 * j) : u4v{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = xl[16 * s + j];
+      xv[s][j] = u4v{v.x, v.y, v.z, v.w};
+    }
 
   // ---- MFMAs over this wave's inputs
   const RbConsts kc = rb_consts();
@@ -164,7 +202,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float xf[8];
-      const u4v w = xv[s][j];
+      const u4v w = has_row ? xv[s][j] : u4v{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xf[2 * i] = __uint_as_float(w[i] << 16);
@@ -207,6 +245,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
 
 __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeArgs a) {
   __shared__ float s_part[kDecodeMaxSlots][16];
+  __shared__ float s_gate[kDecodeMaxSlots];
+  __shared__ f4 s_h[kDecodeMaxSlots * kSpan / 4];  // this token's h, every slot
   const int tid = threadIdx.x, lane = tid & 63, j = tid >> 6;  // wave j: slot j (j == k: shared)
   const int k = a.k, d = a.d, chunks = d / 16;
   const int t = blockIdx.x / chunks, cc = blockIdx.x - t * chunks;
@@ -214,36 +254,48 @@ __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeA
   const bool shared = j == k;
   const int fe = shared ? a.f_sh : a.f;
 
-  // gates of this token, requested before anything else (used at the end)
-  __shared__ float s_gate[kDecodeMaxSlots];
-  if (tid < k) s_gate[tid] = a.gates[t * k + tid];
+  // Requests, all before any use: this slot's expert and gate, then the
+  // token's h rows ((k + 1) x 512 fp32: two 16-byte chunks per thread),
+  // then the slot's weights (which need the expert).
+  const int jr = shared ? 0 : j;
+  const int e_slot = a.ids[t * k + jr];
+  const float g_slot = a.gates[t * k + jr];
+  const f4 *hsrc = reinterpret_cast<const f4 *>(a.h + (int64_t)t * (k + 1) * a.fmax);
+  const f4 h0 = hsrc[tid], h1 = hsrc[tid + 64 * (k + 1)];
 
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  const int e = shared ? 0 : e_slot;
+  const uint32_t *wq = shared ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
+  const uint16_t *wsc = shared ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
+  const uint16_t *wbi = shared ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
+  const int n = 16 * cc + c16;
+  u4v code[kSteps], sw, bw;
   if (fe > 0) {  // fe == kSpan
-    const int e = shared ? 0 : a.ids[t * k + j];
-    const uint32_t *wq = shared ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
-    const uint16_t *wsc = shared ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
-    const uint16_t *wbi = shared ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
-    const int n = 16 * cc + c16;
-    u4v code[kSteps];
     const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + 4 * kq;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) code[s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
-    const u4v sw = *reinterpret_cast<const u4v *>(wsc + (int64_t)n * (kSpan / 64));
-    const u4v bw = *reinterpret_cast<const u4v *>(wbi + (int64_t)n * (kSpan / 64));
-    // activations: row 0 of the tile is this token's h for slot j
-    const float *hr = a.h + ((int64_t)t * (k + 1) + j) * a.fmax + 32 * kq;
+    sw = *reinterpret_cast<const u4v *>(wsc + (int64_t)n * (kSpan / 64));
+    bw = *reinterpret_cast<const u4v *>(wbi + (int64_t)n * (kSpan / 64));
+  }
+  s_h[tid] = h0;
+  s_h[tid + 64 * (k + 1)] = h1;
+  __syncthreads();
+
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  if (fe > 0) {
+    // activations: row 0 of the tile is this token's h for slot j (lanes
+    // c16 == 0); the other rows are zero
+    const f4 *hr = s_h + (j * kSpan + 32 * kq) / 4;
     rb_h8 hv[kSteps][4];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float hf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (c16 == 0) {
-          const f4 h0 = *reinterpret_cast<const f4 *>(hr + 128 * s + 8 * q);
-          const f4 h1 = *reinterpret_cast<const f4 *>(hr + 128 * s + 8 * q + 4);
-          hf[0] = h0[0]; hf[1] = h0[1]; hf[2] = h0[2]; hf[3] = h0[3];
-          hf[4] = h1[0]; hf[5] = h1[1]; hf[6] = h1[2]; hf[7] = h1[3];
+        const f4 lo = hr[32 * s + 2 * q], hi = hr[32 * s + 2 * q + 1];
+        float hf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hf[i] = c16 == 0 ? lo[i] : 0.f;
+          hf[4 + i] = c16 == 0 ? hi[i] : 0.f;
         }
         hv[s][q] = rb_perm8(hf);
       }
@@ -258,6 +310,7 @@ __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeA
   }
   // row 0, column c16 of the tile sits in lane (c16, kq = 0), element 0
   if (kq == 0) s_part[j][c16] = acc[0];
+  if (lane == 0 && !shared) s_gate[j] = g_slot;
   __syncthreads();
   if (tid < 16) {
     float y = 0.f;
@@ -279,11 +332,20 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start
                          hipEvent_t dn_stop) {
   const int vpl = (a.E + 63) / 64;
   const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
-  if (vpl <= 1)       hipExtLaunchKernelGGL(decode_gu_kernel<1>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
-  else if (vpl <= 2)  hipExtLaunchKernelGGL(decode_gu_kernel<2>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
-  else if (vpl <= 4)  hipExtLaunchKernelGGL(decode_gu_kernel<4>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
-  else if (vpl <= 8)  hipExtLaunchKernelGGL(decode_gu_kernel<8>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
-  else                hipExtLaunchKernelGGL(decode_gu_kernel<16>, g1, b1, 0, s, gu_start, gu_stop, 0, a);
+  const size_t xlds = (size_t)a.T * a.d * 2;  // the call's activations
+  if (a.T == 1) {
+    if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 4)  hipExtLaunchKernelGGL((decode_gu_kernel<4, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 8)  hipExtLaunchKernelGGL((decode_gu_kernel<8, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else                hipExtLaunchKernelGGL((decode_gu_kernel<16, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+  } else {
+    if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 4)  hipExtLaunchKernelGGL((decode_gu_kernel<4, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else if (vpl <= 8)  hipExtLaunchKernelGGL((decode_gu_kernel<8, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+    else                hipExtLaunchKernelGGL((decode_gu_kernel<16, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 g2(a.T * (a.d / 16)), b2(64 * (a.k + 1));

@@ -70,11 +70,15 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
 // lanes' heads, after which the winning lane shifts its list up by one.
 template <int VPL>
 __device__ __forceinline__ void topk_wave(const float *row, int E, int k, int lane, int &my_id, float &my_gate) {
+  // every load is unconditional (clamped index) so all are in flight at once
+  float v[VPL];
+#pragma unroll
+  for (int r = 0; r < VPL; ++r) v[r] = row[min(lane + 64 * r, E - 1)];
   uint64_t key[VPL];
 #pragma unroll
   for (int r = 0; r < VPL; ++r) {
     const int e = lane + 64 * r;
-    key[r] = e < E ? make_key(row[e], e) : 0ull;
+    key[r] = e < E ? make_key(v[r], e) : 0ull;
   }
   // descending insertion sort of the lane's keys (VPL <= 16, unrolled)
 #pragma unroll
