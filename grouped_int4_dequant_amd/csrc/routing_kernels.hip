@@ -132,9 +132,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __syncthreads();
   for (int c = threadIdx.x * 8; c < a.d; c += kThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j)
-      add_f16x8(acc, *reinterpret_cast<const uint4 *>(a.o + (int64_t)s_pos[j] * a.d + c), s_w[j]);
-    if (a.o_sh) add_f16x8(acc, *reinterpret_cast<const uint4 *>(a.o_sh + (int64_t)t * a.d + c), 1.f);
+    // eight rows at a time, all requested before the first is added
+    // (clamped: past k the last row again, not added); slot order kept
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const uint4 *>(a.o + (int64_t)s_pos[min(j0 + u, k - 1)] * a.d + c);
+      uint4 vs = make_uint4(0u, 0u, 0u, 0u);
+      if (a.o_sh && j0 + 8 >= k) vs = *reinterpret_cast<const uint4 *>(a.o_sh + (int64_t)t * a.d + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) add_f16x8(acc, v[u], s_w[j0 + u]);
+      if (a.o_sh && j0 + 8 >= k) add_f16x8(acc, vs, 1.f);
+    }
     float4 *dst = reinterpret_cast<float4 *>(a.y + (int64_t)t * a.d + c);
     dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -184,7 +195,16 @@ __global__ __launch_bounds__(kThreads) void count_kernel(ScanArgs a) {
   const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
   for (int e = threadIdx.x; e < E; e += kThreads) s_cnt[e] = 0;
   __syncthreads();
-  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads) atomicAdd(&s_cnt[a.topk_ids[idx]], 1);
+  // four ids per thread at a time, all requested before the first is used
+  // (clamped: past the end the last id again, not counted)
+  for (int64_t base = lo + threadIdx.x; base < hi; base += 4 * kThreads) {
+    int ids[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ids[u] = a.topk_ids[min(base + (int64_t)u * kThreads, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (base + (int64_t)u * kThreads < hi) atomicAdd(&s_cnt[ids[u]], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) a.chunk_counts[(int64_t)c * E + e] = s_cnt[e];
 }
@@ -207,15 +227,32 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   const int64_t tk = (int64_t)T * k;
   const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
 
+  // The first kIdCache ids of this thread's pairs (lo + tid + u * kThreads)
+  // are requested first and kept for both passes below; every load here is
+  // unconditional (clamped index), so none waits on another.
+  constexpr int kIdCache = 4;
+  int idc[kIdCache];
+  if (c < C) {
+#pragma unroll
+    for (int u = 0; u < kIdCache; ++u) idc[u] = a.topk_ids[min(lo + threadIdx.x + (int64_t)u * kThreads, hi - 1)];
+  }
+  auto pair_id = [&](int u, int64_t idx) -> int {
+    int id = 0;
+#pragma unroll
+    for (int q = 0; q < kIdCache; ++q)
+      if (u == q) id = idc[q];
+    return u < kIdCache ? id : a.topk_ids[idx];
+  };
+
   for (int e = threadIdx.x; e < E; e += kThreads) {
     int tot = 0, pre = 0;
     for (int c0 = 0; c0 < C; c0 += 16) {  // sixteen independent loads in flight
       int v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? a.chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < 16; ++u) v[u] = a.chunk_counts[(int64_t)min(c0 + u, C - 1) * E + e];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        tot += v[u];
+        tot += c0 + u < C ? v[u] : 0;
         pre += c0 + u < c ? v[u] : 0;
       }
     }
@@ -225,15 +262,19 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
     s_mask[e] = 0ull;
   }
   __syncthreads();
-  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads)
-    atomicOr(&s_mask[a.topk_ids[idx]], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+  {
+    int u = 0;
+    for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads, ++u)
+      atomicOr(&s_mask[pair_id(u, idx)], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+  }
   const int total = block_exclusive_scan(s_off, E, s_scratch);  // == T*k (syncs inside)
 
   // stable scatter of this sub-chunk's (token, slot) pairs
-  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads) {
+  int u = 0;
+  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads, ++u) {
     const int t = (int)(idx / k);
     const int tl = t - c * kSubChunk;
-    const int e = a.topk_ids[idx];
+    const int e = pair_id(u, idx);
     const uint64_t m = s_mask[e];
     const uint64_t below = tl == 0 ? 0ull : (m & ((1ull << tl) - 1ull));
     const int pos = s_off[e] + s_pre[e] + __popcll(below);
