@@ -98,7 +98,8 @@ def parse():
                          "(a known-size kernel for calibrating hardware byte counters; 0: none)")
     ap.add_argument("--ablations", type=str, default="",
                     help="comma-separated token counts: also time the layer's ablation forms "
-                         "(16-row work units; routing built on the host) at each (e.g. 512,2048)")
+                         "(16-row work units; routing built on the host; weights expanded in memory "
+                         "before the GEMMs) at each (e.g. 512,2048)")
     return ap.parse_args()
 
 
@@ -241,6 +242,9 @@ def main():
 def bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream, tokens, steps, warmup):
     """Wall-clock microseconds per call of each ablation form over the first T
     tokens of the benchmark input, calls back to back on one stream."""
+    need = max(moe.ablation_workspace_bytes(T, layer, v) for T in tokens for v in moe.ABLATIONS)
+    if ws.numel() < need:
+        ws = moe.alloc_workspace(need, x.device)
     res = {}
     for T in tokens:
         if not 0 < T <= x.shape[0]:

@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
                                                    ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P,
                                                    _I32]
         lib.moe_layer_forward_ablation.restype = ctypes.c_int
+        lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
+        lib.moe_ablation_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_prefill_chunked.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
@@ -238,7 +240,14 @@ def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
     return y
 
 
-ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2}
+ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2, "unfused": 3}
+
+
+def ablation_workspace_bytes(T: int, layer: Layer, variant: str) -> int:
+    n = load().moe_ablation_workspace_bytes(T, ctypes.byref(layer.c), ABLATIONS[variant])
+    if n == 0:
+        raise ValueError("invalid layer, token count or ablation")
+    return n
 
 
 def layer_forward_ablation(layer: Layer, x: torch.Tensor, logits: torch.Tensor, variant: str,
@@ -246,13 +255,13 @@ def layer_forward_ablation(layer: Layer, x: torch.Tensor, logits: torch.Tensor, 
                            routing: Optional[Dict[str, torch.Tensor]] = None,
                            ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """moe_layer_forward_ablation: the prefill sequence with one of the pages'
-    ablations ("none", "tile16", "host_routing"); measurement only."""
+    ablations ("none", "tile16", "host_routing", "unfused"); measurement only."""
     T = x.shape[0]
     _need(x, "x", torch.bfloat16, (T, layer.d))
     _need(logits, "logits", torch.float32, (T, layer.E))
     y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
     _need(y, "y", torch.float32, (T, layer.d))
-    ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+    ws = alloc_workspace(ablation_workspace_bytes(T, layer, variant), x.device) if ws is None else ws
     rs = _routing_struct(routing) if routing is not None else None
     _check(load().moe_layer_forward_ablation(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
                                              y.data_ptr(), ctypes.byref(rs) if rs is not None else None,

@@ -48,6 +48,7 @@
 //            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
 
 #include "moe_internal.h"
+#include "rebuild_device.h"
 
 #include <hip/hip_fp16.h>
 
@@ -76,6 +77,13 @@ constexpr int kTabStride = kColsMax + 16;          // dwords per group row of th
 template <int CB>
 struct BStage {
   u4 q[CB];            // 4 code words (32 codes) per column block
+};
+
+// Weights already expanded to fp16 in device memory (the unfused ablation):
+// the lane's 32 weights of each column block as four 8-weight chunks.
+template <int CB>
+struct XStage {
+  u4 q[CB][4];
 };
 
 __device__ __forceinline__ uint32_t pack_scale_bias(uint32_t s_bits, uint32_t b_bits) {
@@ -117,7 +125,7 @@ struct Unit {
 
 // NRB = 16-row MFMA blocks of the unit (1..6), fixed at compile time so a K
 // step is one branch-free block the compiler can schedule as a whole.
-template <int MODE, bool AF16, int NRB, int CB>
+template <int MODE, bool AF16, bool WX, int NRB, int CB>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
   constexpr int kMaxRB = NRB;
@@ -126,6 +134,9 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   constexpr int kCols = 16 * CB * kWaves;    // weight rows (output columns) of this item
   constexpr int kRB32 = (NRB + 1) / 2;                                    // 32-row blocks staged
   constexpr int kSlabs = (32 * kRB32 / kSlabRows + kWaves - 1) / kWaves;  // A stores per wave
+  // WX: the weights come expanded (fp16, each 8-run in the rebuild order)
+  // from P.Wx; no codes, no table, no rebuild.
+  typedef typename std::conditional<WX, XStage<CB>, BStage<CB>>::type Stage;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int N = P.N, K = P.K, G = K >> 6;
@@ -181,12 +192,23 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // first input of this lane's quarter at step s (valid iff < K)
   auto lane_k0 = [&](int s) { return kKStep * s + 32 * kq; };
 
-  auto load_b = [&](BStage<kCB> &st, int s) {
+  auto load_b = [&](Stage &st, int s) {
     const int k0 = lane_k0(s);
     const int kc = k0 < K ? k0 : 0;
+    if constexpr (WX) {
+      // weight row of each column block: N * K elements per expert, which
+      // the host keeps below 2^31
+      const uint16_t *wx = P.Wx + (int64_t)U.e * P.wx_estride;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-      st.q[cb] = *reinterpret_cast<const u4 *>(wq + (uint32_t)(b_row[cb] + (kc >> 3)));
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          st.q[cb][j] = *reinterpret_cast<const u4 *>(wx + ((uint32_t)ncol[cb] * (uint32_t)K + (uint32_t)(kc + 8 * j)));
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        st.q[cb] = *reinterpret_cast<const u4 *>(wq + (uint32_t)(b_row[cb] + (kc >> 3)));
+    }
   };
 
   // Scale/bias table for groups [32 gc, 32 gc + 32): tab[g][c] holds
@@ -301,13 +323,13 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   const uint32_t m_lo = vgpr_const(0x000F000Fu), m_hi = vgpr_const(0x00F000F0u);
   const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
 
-  auto compute = [&](const BStage<kCB> &st, int s, int buf) {
+  auto compute = [&](const Stage &st, int s, int buf) {
     const int k0 = lane_k0(s);
     const bool kvalid = k0 < K;
     const int gt = ((k0 >> 6) & (kTabGroups - 1)) * kTabStride;  // group row in the table
     h2 s1[kCB], s16[kCB], cc[kCB];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
+    for (int cb = 0; cb < kCB && !WX; ++cb) {
       const uint32_t tv = kvalid ? tab[gt + tcol[cb]] : 0u;
       const h2 sc = __builtin_bit_cast(h2, tv);
       s1[cb] = h2{sc[0], sc[0]};
@@ -319,6 +341,10 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
     // rebuild the 32 codes of quarter-step j for column block cb
     auto rebuild = [&](int j, int cb) -> h8 {
+      // expanded weights: inputs past K (the last step's loads were clamped
+      // to the row start) contribute zero, as the zero table does below
+      if constexpr (WX) return kvalid ? __builtin_bit_cast(h8, st.q[cb][j]) : h8{};
+      else {
       const uint32_t w = st.q[cb][j];
       const uint32_t w8 = w >> 8;
       // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
@@ -331,6 +357,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
       const h2 w2 = __builtin_elementwise_fma(t2, s1[cb], cc[cb]);
       const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
       return h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+      }
     };
     auto read_a = [&](int j, int rb) -> h8 {
       const int aoff = 16 * ((4 * kq + j) ^ c16);
@@ -368,9 +395,9 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // requested, step s is computed, then A(s+1) is written to LDS. Loads are
   // issued unconditionally (clamped to the last step) so every step has the
   // same number in flight and the compiler's wait counts stay exact.
-  auto body = [&](int s, const BStage<kCB> &cur, BStage<kCB> &nxt) {
+  auto body = [&](int s, const Stage &cur, Stage &nxt) {
     lds_barrier();
-    if (s > 0 && s < steps && (s & 15) == 0) {  // next 2048 inputs: next table chunk
+    if (!WX && s > 0 && s < steps && (s & 15) == 0) {  // next 2048 inputs: next table chunk
       fill_table(s >> 4);
       lds_barrier();
     }
@@ -381,8 +408,8 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     store_a((s + 1) & 1);
   };
 
-  BStage<kCB> b0, b1;
-  fill_table(0);
+  Stage b0, b1;
+  if (!WX) fill_table(0);
   load_a(0);
   load_b(b0, 0);
   store_a(0);
@@ -436,7 +463,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   }
 }
 
-template <int MODE, bool AF16>
+template <int MODE, bool AF16, bool WX>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
   __shared__ uint32_t tab[kTabGroups * kTabStride];
@@ -492,23 +519,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
   __syncthreads();
 
   // half-width items: the same code with half the column blocks per wave
-  if (narrow) {
+  // (always, for expanded weights: their stages take four times the registers)
+  if (WX || narrow) {
     switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 1: run_unit<MODE, AF16, WX, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, WX, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, WX, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, WX, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, WX, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, WX, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
     }
   } else {
     switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, 1, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, 2, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, 3, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, 4, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, 5, kCBFull>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, 6, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 1: run_unit<MODE, AF16, WX, 1, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, WX, 2, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, WX, 3, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, WX, 4, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, WX, 5, kCBFull>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, WX, 6, kCBFull>(P, U, lds, s_arow, tab); break;
     }
   }
 }
@@ -516,19 +544,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start,
-                       hipEvent_t stop) {
+                       hipEvent_t stop, bool expanded) {
   const dim3 grid(a.total_wg), block(kGemmThreads);
   if (a.total_wg == 0) return hipSuccess;
-  if (a_f16) {
+  if (expanded) {  // layer GEMMs over expanded weights (unfused ablation)
     switch (mode) {
-      case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true>), grid, block, 0, s, start, stop, 0, a); break;
-      case kStoreH: hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true>), grid, block, 0, s, start, stop, 0, a); break;
-      default: hipExtLaunchKernelGGL((gemm_kernel<kStoreC, true>), grid, block, 0, s, start, stop, 0, a); break;
+      case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, true>), grid, block, 0, s, start, stop, 0, a); break;
+      case kStoreH: hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, true>), grid, block, 0, s, start, stop, 0, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (a_f16) {
+    switch (mode) {
+      case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, start, stop, 0, a); break;
+      case kStoreH: hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false>), grid, block, 0, s, start, stop, 0, a); break;
+      default: hipExtLaunchKernelGGL((gemm_kernel<kStoreC, true, false>), grid, block, 0, s, start, stop, 0, a); break;
     }
   } else {
     // bf16 activations: stand-alone GEMM over block-map entries (<= 32 rows)
-    hipExtLaunchKernelGGL((gemm_kernel<kStoreC, false>), grid, block, 0, s, start, stop, 0, a);
+    hipExtLaunchKernelGGL((gemm_kernel<kStoreC, false, false>), grid, block, 0, s, start, stop, 0, a);
   }
+  return hipGetLastError();
+}
+
+// Weights of `rows` rows of K inputs (all experts of a projection, stored
+// back to back) rebuilt once into fp16 in device memory, each 8-run in the
+// rebuild order, with the same arithmetic as the GEMM's on-chip rebuild.
+__global__ __launch_bounds__(256) void expand_kernel(const uint32_t *q, const uint16_t *sc, const uint16_t *bi,
+                                                     int64_t words, int K, uint16_t *out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= words) return;
+  const int kw = K >> 3, G = K >> 6;
+  const int64_t row = i / kw;
+  const int wi = (int)(i - row * kw);
+  const int64_t gi = row * G + (wi >> 3);
+  const uint32_t packed = rb_pack_scale_bias(sc[gi], bi[gi]);
+  const rb_h8 w = rb_rebuild(q[i], packed, rb_consts());
+  reinterpret_cast<rb_h8 *>(out)[i] = w;
+}
+
+hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int64_t rows, int K,
+                         uint16_t *out, hipStream_t s) {
+  const int64_t words = rows * (K / 8);
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, s, q, sc, bi, words, K, out);
   return hipGetLastError();
 }
 

@@ -53,7 +53,16 @@ struct FwdOptions {
   int ntail = 0;              // routed units run as half-width items at the end
   bool host_routing = false;  // counts, offsets, scatter, block map and work list built on the host
   bool few_token_form = true; // calls of at most 8 tokens take the two-kernel decode form
+  bool unfused = false;       // weights expanded to fp16 in the workspace, then read by the GEMMs
 };
+
+// Unfused ablation: fp16 buffer for one projection's expanded weights (all
+// routed experts, then the shared expert), reused by gate/up and down.
+size_t expand_bytes(const moe_layer_t *L) {
+  const int64_t gu = (int64_t)L->E * 2 * L->f * L->d + (int64_t)2 * L->f_sh * L->d;
+  const int64_t dn = (int64_t)L->E * L->d * L->f + (int64_t)L->d * L->f_sh;
+  return (size_t)round_up(2 * std::max(gu, dn), kAlign);
+}
 
 int check_layer(const moe_layer_t *L) {
   if (!L) return MOE_EINVAL;
@@ -257,9 +266,10 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
                 hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true}) {
   const size_t need = carve_layer(T, L, nullptr, nullptr);
-  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (ws_bytes < need + (opt.unfused ? expand_bytes(L) : 0)) return MOE_EWORKSPACE;
   Workspace w;
   carve_layer(T, L, static_cast<char *>(ws), &w);
+  uint16_t *wx = opt.unfused ? reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + need) : nullptr;
   const moe_routing_t &rt = routing ? *routing : w.rt;
   const int d = L->d, f = L->f, E = L->E, k = L->k, fs = L->f_sh;
   // The GEMM addresses the layer's fp16 activation buffers and one expert's
@@ -307,6 +317,15 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   if (st != MOE_OK) return st;
 
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
+  // (unfused ablation: weights first expanded into the workspace, items of
+  // 128 columns of h)
+  const int hcols = opt.unfused ? 128 : 256;
+  if (opt.unfused) {
+    st = hip_status(launch_expand(L->gu_q, L->gu_s, L->gu_b, (int64_t)E * 2 * f, d, wx, s));
+    if (st == MOE_OK && fs > 0)
+      st = hip_status(launch_expand(L->sh_gu_q, L->sh_gu_s, L->sh_gu_b, 2 * fs, d, wx + (int64_t)E * 2 * f * d, s));
+    if (st != MOE_OK) return st;
+  }
   GemmArgs g1{};
   int nwg = 0, np = 0;
   if (fs > 0) {
@@ -315,8 +334,9 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->sh_gu_q; p.Ws = L->sh_gu_s; p.Wb = L->sh_gu_b;
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = 2 * fs; p.K = d;
+    p.Wx = wx ? wx + (int64_t)E * 2 * f * d : nullptr; p.wx_estride = 0;
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
-    p.nslices = (int)ceil_div(fs, 256);
+    p.nslices = (int)ceil_div(fs, hcols);
     p.wg_begin = nwg;
     p.H = w.h_sh; p.ldh = fs;
     nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
@@ -327,8 +347,9 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->gu_q; p.Ws = L->gu_s; p.Wb = L->gu_b;
     p.wq_estride = (int64_t)2 * f * (d / 8); p.ws_estride = (int64_t)2 * f * (d / 64);
     p.N = 2 * f; p.K = d;
+    p.Wx = wx; p.wx_estride = (int64_t)2 * f * d;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
-    p.nslices = (int)ceil_div(f, 256);
+    p.nslices = (int)ceil_div(f, hcols);
     p.ntail = opt.ntail;
     p.wg_begin = nwg;
     p.H = w.h; p.ldh = f;
@@ -337,8 +358,15 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   }
   g1.nprob = np;
   g1.total_wg = nwg;
-  st = hip_status(launch_gemm(g1, kSwiGLU, true, s, nullptr, ev ? ev[3] : nullptr));
+  st = hip_status(launch_gemm(g1, kSwiGLU, true, s, nullptr, ev ? ev[3] : nullptr, opt.unfused));
   if (st != MOE_OK) return st;
+  const int ocols = opt.unfused ? 256 : 512;
+  if (opt.unfused) {
+    st = hip_status(launch_expand(L->dn_q, L->dn_s, L->dn_b, (int64_t)E * d, f, wx, s));
+    if (st == MOE_OK && fs > 0)
+      st = hip_status(launch_expand(L->sh_dn_q, L->sh_dn_s, L->sh_dn_b, d, fs, wx + (int64_t)E * d * f, s));
+    if (st != MOE_OK) return st;
+  }
 
   // down projection into fp16 expert outputs, then the weighted combine
   GemmArgs g2{};
@@ -350,8 +378,9 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->sh_dn_q; p.Ws = L->sh_dn_s; p.Wb = L->sh_dn_b;
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = d; p.K = fs;
+    p.Wx = wx ? wx + (int64_t)E * d * f : nullptr; p.wx_estride = 0;
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
-    p.nslices = (int)ceil_div(d, 512);
+    p.nslices = (int)ceil_div(d, ocols);
     p.wg_begin = nwg;
     p.H = w.o_sh; p.ldh = d;
     nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
@@ -362,8 +391,9 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.Wq = L->dn_q; p.Ws = L->dn_s; p.Wb = L->dn_b;
     p.wq_estride = (int64_t)d * (f / 8); p.ws_estride = (int64_t)d * (f / 64);
     p.N = d; p.K = f;
+    p.Wx = wx; p.wx_estride = (int64_t)d * f;
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
-    p.nslices = (int)ceil_div(d, 512);
+    p.nslices = (int)ceil_div(d, ocols);
     p.ntail = opt.ntail;
     p.wg_begin = nwg;
     p.H = w.o; p.ldh = d;
@@ -371,7 +401,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   }
   g2.nprob = np;
   g2.total_wg = nwg;
-  st = hip_status(launch_gemm(g2, kStoreH, true, s));
+  st = hip_status(launch_gemm(g2, kStoreH, true, s, nullptr, nullptr, opt.unfused));
   if (st != MOE_OK) return st;
 
   return enqueue_combine(T, d, k, w.o, fs > 0 ? w.o_sh : nullptr, rt, y, s, ev);
@@ -397,6 +427,12 @@ size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {
   if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->k > L->E || L->f_sh < 0) return 0;
   if (L->E > MOE_MAX_EXPERTS || L->k > kMaxTopK || L->d % 64 || L->f % 64 || L->f_sh % 64) return 0;
   return carve_layer(T, L, nullptr, nullptr);
+}
+
+size_t moe_ablation_workspace_bytes(int32_t T, const moe_layer_t *L, int32_t variant) {
+  const size_t base = moe_workspace_bytes(T, L);
+  if (base == 0 || variant < MOE_ABLATION_NONE || variant > MOE_ABLATION_UNFUSED) return 0;
+  return base + (variant == MOE_ABLATION_UNFUSED ? expand_bytes(L) : 0);
 }
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_routing_t *out,
@@ -475,6 +511,7 @@ int moe_layer_forward_ablation(const moe_layer_t *L, const uint16_t *x, const fl
     case MOE_ABLATION_NONE: break;
     case MOE_ABLATION_TILE16: opt.unit_rows = 16; opt.ntail = 0; break;
     case MOE_ABLATION_HOST_ROUTING: opt.host_routing = true; break;
+    case MOE_ABLATION_UNFUSED: opt.unfused = true; opt.ntail = 0; break;
     default: return MOE_EINVAL;
   }
   int st = check_layer(L);

@@ -78,6 +78,8 @@ struct GemmProblem {
   const uint32_t *Wq;        // expert 0 packed codes [N][K/8]
   const uint16_t *Ws, *Wb;   // expert 0 scales / biases [N][K/64]
   int64_t wq_estride, ws_estride;  // per-expert element strides
+  const uint16_t *Wx;        // expanded fp16 weights [N][K] of expert 0 (unfused ablation only)
+  int64_t wx_estride;
   int N, K;
   const int32_t *units;      // [*][3] (expert, first row, rows <= 128); nullptr: implicit
   const int32_t *num_units;  // device count of units
@@ -99,8 +101,13 @@ struct GemmArgs {
 
 // a_f16: the A operand is fp16 in the permuted-run layout (fast path);
 // otherwise bf16 in natural order, converted while staging.
+// expanded: the weights are read expanded from Wx (unfused ablation; modes
+// kSwiGLU and kStoreH).
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr);
+                       hipEvent_t stop = nullptr, bool expanded = false);
+// Unfused ablation: weights of rows x K expanded into fp16 (rebuild order).
+hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int64_t rows, int K,
+                         uint16_t *out, hipStream_t s);
 
 // ------------------------------------------------------------------ decode
 // Calls of at most kDecodeMaxT tokens run as two kernels (decode_kernels.hip):

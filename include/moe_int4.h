@@ -217,9 +217,12 @@ int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float
 /*
  * The layer with one of the pages' ablations, for measurement only (Lily-EN
  * "Prefill: Keep Weights Packed, Keep Routing on the GPU" and Lily-ES
- * "Precarga...": routing kept on the GPU and 32-row rather than 16-row
- * tiles are two of the changes they measure). Always takes the prefill form
- * (also for T <= 8); otherwise as moe_layer_forward, with the same results.
+ * "Precarga...": dequantisation fused into the GEMM, routing kept on the GPU
+ * and 32-row rather than 16-row tiles are the changes they measure). Always
+ * takes the prefill form (also for T <= 8); otherwise as moe_layer_forward,
+ * with the same results (bit for bit: the GEMMs accumulate in the same
+ * order and the unfused form expands weights with the same arithmetic).
+ * ws_bytes must be at least moe_ablation_workspace_bytes(T, L, variant).
  *   MOE_ABLATION_NONE          the default prefill sequence
  *   MOE_ABLATION_TILE16        GEMM work units of at most 16 rows (instead of
  *                              96), so each rebuilt weight feeds 16 rows
@@ -228,11 +231,21 @@ int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float
  *                              offsets, scatter, block map and work list and
  *                              copies them back: synchronises the stream
  *                              twice and allocates host memory
+ *   MOE_ABLATION_UNFUSED       every expert's weights (routed and shared) are
+ *                              first expanded to fp16 in the workspace, one
+ *                              projection at a time, and the grouped GEMMs
+ *                              read the expanded weights (no on-chip rebuild)
  * Errors: as moe_layer_forward; MOE_EINVAL for an unknown variant.
  */
 #define MOE_ABLATION_NONE 0
 #define MOE_ABLATION_TILE16 1
 #define MOE_ABLATION_HOST_ROUTING 2
+#define MOE_ABLATION_UNFUSED 3
+/* Workspace bytes for moe_layer_forward_ablation: moe_workspace_bytes(T, L)
+ * plus, for MOE_ABLATION_UNFUSED, an fp16 buffer for the larger projection's
+ * expanded weights (2 x max(E*2f*d + 2 f_sh*d, E*d*f + d*f_sh) bytes). 0 for
+ * an invalid layer, T or variant. Host only. */
+size_t moe_ablation_workspace_bytes(int32_t T, const moe_layer_t *L, int32_t variant);
 int moe_layer_forward_ablation(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
                                float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
                                hipStream_t stream, int32_t variant);

@@ -98,8 +98,15 @@ def test_ablation_entry_point_validates_like_the_forward():
         assert abl(0x1000, 0x1000, 0, 0x1000, None, 0x1000, 0, None, v) == B.MOE_OK
         assert abl(None, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, v) == B.MOE_EINVAL
         assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 100, None, v) == B.MOE_EWORKSPACE
-    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, 3) == B.MOE_EINVAL
-    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None, -1) == B.MOE_EINVAL
+    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 40, None, 4) == B.MOE_EINVAL
+    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 40, None, -1) == B.MOE_EINVAL
+    # the unfused form needs room for one projection's expanded weights
+    base = lib.moe_workspace_bytes(16, ctypes.byref(L))
+    assert lib.moe_ablation_workspace_bytes(16, ctypes.byref(L), 0) == base
+    big = lib.moe_ablation_workspace_bytes(16, ctypes.byref(L), 3)
+    assert big - base >= 2 * (256 * 1024 * 2048 + 1024 * 2048)
+    assert lib.moe_ablation_workspace_bytes(16, ctypes.byref(L), 4) == 0
+    assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, big - 1, None, 3) == B.MOE_EWORKSPACE
 
 
 def test_route_and_gemm_reject_bad_arguments():
