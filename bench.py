@@ -226,6 +226,7 @@ def main():
                   "weight_gbps": touched_bytes / (ms_per_step * 1e-3) / 1e9},
     }
 
+    out["router"] = bench_router(moe, S, torch, x, sh, args.steps)
     if args.decode_steps > 0:
         out["decode_t1"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events)
     if args.ablations:
@@ -237,6 +238,27 @@ def main():
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def bench_router(moe, S, torch, x, sh, steps):
+    """The router projection (logits = x W_r^T, bf16 in, fp32 out) over the
+    benchmark's tokens with seeded N(0, 1/d) router weights: GPU time per
+    call from events around back-to-back calls."""
+    T = x.shape[0]
+    w = S.draw_router(sh.E, sh.d, np.random.default_rng(1234))
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(x.device)
+    lg = torch.empty((T, sh.E), dtype=torch.float32, device=x.device)
+    for _ in range(5):
+        moe.router_logits(x, wt, logits=lg)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        moe.router_logits(x, wt, logits=lg)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"T": T, "d": sh.d, "E": sh.E, "us_per_call": us,
+            "tflops": 2.0 * T * sh.d * sh.E / (us * 1e-6) / 1e12}
 
 
 def bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream, tokens, steps, warmup):

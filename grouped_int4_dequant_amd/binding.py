@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
                                                    ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P,
                                                    _I32]
         lib.moe_layer_forward_ablation.restype = ctypes.c_int
+        lib.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
+        lib.moe_router_logits.restype = ctypes.c_int
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
         lib.moe_ablation_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_prefill_chunked.restype = ctypes.c_int
@@ -238,6 +240,21 @@ def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
                                     ws.data_ptr(), ws.numel(), _stream(stream)),
            "moe_layer_forward")
     return y
+
+
+def router_logits(x: torch.Tensor, w_r: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """moe_router_logits: logits fp32 [T][E] = x W_r^T from bf16 x [T][d] and
+    bf16 W_r [E][d]."""
+    T, d = x.shape
+    E = w_r.shape[0]
+    _need(x, "x", torch.bfloat16, (T, d))
+    _need(w_r, "w_r", torch.bfloat16, (E, d))
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if logits is None else logits
+    _need(logits, "logits", torch.float32, (T, E))
+    _check(load().moe_router_logits(x.data_ptr(), T, d, w_r.data_ptr(), E, logits.data_ptr(), _stream(stream)),
+           "moe_router_logits")
+    return logits
 
 
 ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2, "unfused": 3}

@@ -435,6 +435,17 @@ size_t moe_ablation_workspace_bytes(int32_t T, const moe_layer_t *L, int32_t var
   return base + (variant == MOE_ABLATION_UNFUSED ? expand_bytes(L) : 0);
 }
 
+int moe_router_logits(const uint16_t *x, int32_t T, int32_t d, const uint16_t *w_r, int32_t E,
+                      float *logits, hipStream_t stream) {
+  if (T < 0 || d < 1 || E < 1) return MOE_EINVAL;
+  if (d % 32 || E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_r || !logits || !aligned16(x) || !aligned16(w_r) || !aligned16(logits)) return MOE_EINVAL;
+  RouterArgs a{};
+  a.x = x; a.w = w_r; a.T = T; a.d = d; a.E = E; a.logits = logits;
+  return hip_status(launch_router(a, stream));
+}
+
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, const moe_routing_t *out,
               void *ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;

@@ -54,6 +54,15 @@ struct ScanArgs {
   int32_t *chunk_counts;        // scratch [ceil(T/64)][E]
 };
 
+// logits[t][e] = sum_k x[t][k] * w[e][k] (bf16 inputs, fp32 accumulation).
+struct RouterArgs {
+  const uint16_t *x;        // bf16 [T][d]
+  const uint16_t *w;        // bf16 [E][d]
+  int T, d, E;
+  float *logits;            // fp32 [T][E]
+};
+hipError_t launch_router(const RouterArgs &a, hipStream_t s);
+
 // Optional events (nullable) are attached to a kernel's dispatch: start at
 // its first wave, stop at its end, with no extra packet between kernels.
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start = nullptr,

@@ -136,6 +136,20 @@ size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L);
 size_t moe_route_workspace_bytes(int32_t T, int32_t E);
 
 /*
+ * Router projection, the step before routing (Lily-EN "Three Workload
+ * Shapes": a router scores every expert per token): logits[t][e] =
+ * sum_k x[t][k] * w_r[e][k]. x bf16 [T][d] and w_r bf16 [E][d] (device, row
+ * major, 16-byte aligned, caller-owned); logits fp32 [T][E] (device, written).
+ * Products are exact in fp32 and accumulate in fp32 in a fixed order, so a
+ * call is deterministic. Errors: MOE_EINVAL (null or unaligned pointer,
+ * T < 0, d < 1, E < 1), MOE_EUNSUPPORTED (d not a multiple of 32, E >
+ * MOE_MAX_EXPERTS, T > MOE_MAX_CALL_TOKENS). T == 0 enqueues nothing. One
+ * kernel; allocates nothing.
+ */
+int moe_router_logits(const uint16_t *x, int32_t T, int32_t d, const uint16_t *w_r, int32_t E,
+                      float *logits, hipStream_t stream);
+
+/*
  * Routing only. logits fp32 [T][E] (device). Fills every field of *out (the
  * struct itself is read on the host; its pointers are device pointers).
  * ws: device workspace of at least moe_route_workspace_bytes(T, E) bytes,

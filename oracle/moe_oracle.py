@@ -8,6 +8,10 @@ inputs and nothing else.
 What it computes, step by step, in the order the pages describe the layer
 (pages keyed below):
 
+  0. router     logits = x W_r^T from bf16 token activations and bf16 router
+                weights (Lily-EN "Three Workload Shapes": the router scores
+                every expert for each token); the layer itself takes logits
+                as an input
   1. unpack     4-bit codes, eight per uint32, low nibble first
   2. dequant    w = s * q + b, one bf16 scale and one bf16 bias per 64
                 consecutive input-dimension weights
@@ -87,6 +91,14 @@ def dequant(words, scale_bits, bias_bits) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- routing ---
+def router_logits(x_bits, w_bits) -> np.ndarray:
+    """Step 0 (Lily-EN "Three Workload Shapes"): the router's score of every
+    expert for every token, logits[t][e] = sum_k x[t][k] * W_r[e][k], from
+    bf16 x [T][d] and bf16 W_r [E][d], in float64 (a library matrix product
+    on exactly widened values)."""
+    return bf16_value(x_bits) @ bf16_value(w_bits).T
+
+
 def topk(logits, k: int) -> np.ndarray:
     """Step 3 (Lily-EN "Three Workload Shapes"): for every token the k experts
     with the largest logits, listed by (logit descending, expert ascending).

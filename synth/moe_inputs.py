@@ -141,6 +141,20 @@ def draw_tokens(T: int, shape: LayerShape, rng: np.random.Generator,
     return logits, x
 
 
+def draw_router(E: int, d: int, rng: np.random.Generator) -> np.ndarray:
+    """Router weights bf16 bits [E][d], N(0, 1/d): with x ~ N(0,1) the logits
+    come out about N(0,1), the distribution the layer workloads draw directly."""
+    return f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+
+
+def make_router_problem(T: int, d: int, E: int, seed: int):
+    """Seeded router-projection inputs: x bf16 bits [T][d] (N(0,1)), then W_r
+    bf16 bits [E][d]."""
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    return x, draw_router(E, d, rng)
+
+
 @dataclasses.dataclass
 class Problem:
     config: Config

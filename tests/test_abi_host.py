@@ -109,6 +109,18 @@ def test_ablation_entry_point_validates_like_the_forward():
     assert abl(0x1000, 0x1000, 16, 0x1000, None, 0x1000, big - 1, None, 3) == B.MOE_EWORKSPACE
 
 
+def test_router_logits_rejects_bad_arguments():
+    lib = moe.load()
+    rl = lib.moe_router_logits
+    assert rl(0x1000, 0, 64, 0x1000, 16, 0x1000, None) == B.MOE_OK          # T == 0: no-op
+    assert rl(None, 4, 64, 0x1000, 16, 0x1000, None) == B.MOE_EINVAL
+    assert rl(0x1000, 4, 64, 0x1008, 16, 0x1000, None) == B.MOE_EINVAL      # unaligned
+    assert rl(0x1000, -1, 64, 0x1000, 16, 0x1000, None) == B.MOE_EINVAL
+    assert rl(0x1000, 4, 48, 0x1000, 16, 0x1000, None) == B.MOE_EUNSUPPORTED  # d % 32
+    assert rl(0x1000, 4, 64, 0x1000, 2048, 0x1000, None) == B.MOE_EUNSUPPORTED
+    assert rl(0x1000, 1 << 20, 64, 0x1000, 16, 0x1000, None) == B.MOE_EUNSUPPORTED
+
+
 def test_route_and_gemm_reject_bad_arguments():
     lib = moe.load()
     r = B.MoeRoutingT(*([0x1000] * 9))

@@ -303,6 +303,58 @@ def test_decode_tied_logits(moe):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, 8), "decode ties")
 
 
+# ------------------------------------------------------------------ router
+def _router_bound(x_bits, w_bits):
+    """Error bound of an fp32 sum of d exact products in any order:
+    (d - 1) * 2^-24 * sum_k |x_k w_k| per logit (the bf16 products are exact
+    in fp32)."""
+    d = x_bits.shape[1]
+    return (d - 1) * 2.0 ** -24 * (np.abs(O.bf16_value(x_bits)) @ np.abs(O.bf16_value(w_bits)).T)
+
+
+@pytest.mark.parametrize("T,d,E", [(2048, 2048, 256), (37, 96, 20), (1, 32, 1), (130, 512, 1024)])
+def test_router_logits_match_oracle(moe, T, d, E):
+    say(f"router T={T} d={d} E={E}")
+    x, w = S.make_router_problem(T, d, E, seed=T + d + E)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    lg = moe.router_logits(xt, wt)
+    lg2 = moe.router_logits(xt, wt)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy().astype(np.float64)
+    ref = O.router_logits(x, w)
+    assert np.array_equal(got, lg2.cpu().numpy()), "router logits differ between calls"
+    err = np.abs(got - ref)
+    bound = _router_bound(x, w)
+    say(f"  max err {err.max():.3e}, max err/bound {np.max(err / np.maximum(bound, 1e-30)):.3f}")
+    assert np.all(err <= bound)
+
+
+def test_router_then_route_matches_oracle_routing(moe):
+    """Logits from the router kernel feed the routing kernels; the picks agree
+    with the oracle's top-k of the exact logits wherever the k-th and
+    (k+1)-th exact logits are further apart than the error bound, and are
+    valid picks (within the bound of the k-th) everywhere."""
+    T, d, E, k = 2048, 2048, 256, 8
+    x, w = S.make_router_problem(T, d, E, seed=5)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    got = moe.route(moe.router_logits(xt, wt), k)
+    torch.cuda.synchronize()
+    ref = O.router_logits(x, w)
+    bound = _router_bound(x, w)
+    ids = got["topk_ids"].cpu().numpy()
+    ref_sorted = -np.sort(-ref, axis=1)
+    clear = (ref_sorted[:, k - 1] - ref_sorted[:, k]) > 2 * bound.max(axis=1)
+    ref_ids = O.topk(ref.astype(np.float32), k)
+    for t in range(T):
+        if clear[t]:
+            assert set(ids[t]) == set(ref_ids[t]), t
+        picked = ref[t, ids[t]]
+        assert np.all(picked >= ref_sorted[t, k - 1] - 2 * bound[t].max()), t
+    say(f"  {int(clear.sum())} of {T} tokens with a clear k-th pick")
+
+
 # ------------------------------------------------------------------ ablations
 ABLATION_SHAPES = [
     # T, d, f, E, k, f_sh

@@ -381,6 +381,51 @@ PIN_TESTS = [test_unpack_hand_words, test_dequant_hand_values, test_dequant_grou
              test_brute_force_tiny_layer, test_sorted_form_matches_token_form]
 
 
+# ---------------------------------------------------------- P0 router ---
+def test_router_one_hot_rows_pick_weight_columns():
+    """x = e_j (one-hot) gives logits[e] = W_r[e][j] exactly."""
+    d, E = 64, 12
+    rng = np.random.default_rng(7)
+    w = S.draw_router(E, d, rng)
+    x = np.zeros((d, d), np.uint16)
+    x[np.arange(d), np.arange(d)] = bf16(1.0)
+    L = O.router_logits(x, w)
+    assert np.array_equal(L, O.bf16_value(w).T)
+
+
+def test_router_brute_force_exact():
+    """A tiny case against exact rational arithmetic of the definition."""
+    from fractions import Fraction
+    x, w = S.make_router_problem(3, 32, 5, seed=11)
+    L = O.router_logits(x, w)
+    xv, wv = O.bf16_value(x), O.bf16_value(w)
+    for t in range(3):
+        for e in range(5):
+            exact = sum(Fraction(float(xv[t, k])) * Fraction(float(wv[e, k])) for k in range(32))
+            assert abs(L[t, e] - float(exact)) <= 1e-14 * max(1.0, abs(float(exact)))
+
+
+def test_router_equivariance_and_scale():
+    """Permuting experts permutes columns; a common permutation of the input
+    dimension changes nothing (up to summation order); doubling x doubles the
+    logits exactly; constant rows give d * c * sum."""
+    x, w = S.make_router_problem(6, 64, 9, seed=12)
+    L = O.router_logits(x, w)
+    pe = np.random.default_rng(1).permutation(9)
+    assert np.array_equal(O.router_logits(x, w[pe]), L[:, pe])
+    pk = np.random.default_rng(2).permutation(64)
+    assert np.allclose(O.router_logits(x[:, pk], w[:, pk]), L, rtol=1e-12, atol=1e-12)
+    x2 = S.f32_to_bf16_bits(2.0 * O.bf16_value(x).astype(np.float32))
+    assert np.array_equal(O.router_logits(x2, w), 2.0 * L)
+    ones = np.full((2, 64), bf16(1.0), np.uint16)
+    c = np.full((3, 64), bf16(0.125), np.uint16)
+    assert np.array_equal(O.router_logits(ones, c), np.full((2, 3), 8.0))
+
+
+PIN_TESTS += [test_router_one_hot_rows_pick_weight_columns, test_router_brute_force_exact,
+              test_router_equivariance_and_scale]
+
+
 def _some_pin_fails():
     for t in PIN_TESTS:
         try:
@@ -435,7 +480,17 @@ def _mut_block_16(cnt, offs, T, k):
     return bm, n + (1 if n else 0)
 
 
+def _mut_router_drops_last_input(x_bits, w_bits):
+    return O.bf16_value(x_bits)[:, :-1] @ O.bf16_value(w_bits)[:, :-1].T
+
+
+def _mut_router_expert_shift(x_bits, w_bits):
+    return O.bf16_value(x_bits) @ np.roll(O.bf16_value(w_bits), 1, axis=0).T
+
+
 @pytest.mark.parametrize("name,fn", [
+    ("router_logits", _mut_router_drops_last_input),
+    ("router_logits", _mut_router_expert_shift),
     ("unpack_int4", _mut_high_nibble_first),
     ("dequant", _mut_no_bias),
     ("dequant", _mut_group_mod),
