@@ -10,12 +10,13 @@
 // tiles). That design targeted Metal tensor ops on bf16; on gfx950 it becomes:
 //
 //   * Work unit: up to 96 rows (three 32-row blocks) of one expert x one
-//     512-column N-slice of the weights. A workgroup is 8 waves (two per
-//     SIMD, at most 256 registers per lane); a wave owns 64 weight rows
+//     256-column N-slice of the weights. A workgroup is 4 waves, one per
+//     SIMD, and two workgroups share a CU (at most 256 registers per lane,
+//     about 65 KiB of LDS each), so one workgroup's barrier waits, prologue
+//     and epilogue overlap the other's MFMAs. A wave owns 64 weight rows
 //     (output columns) as four 16-column MFMA blocks and every row of the
-//     unit, so each rebuilt weight feeds every row of the unit, and the
-//     unit's activation rows are staged once for 512 columns. Units come
-//     largest first; the last few (a problem's ntail) run as 256-column
+//     unit, so each rebuilt weight feeds every row of the unit. Units come
+//     largest first; the last few (a problem's ntail) run as 128-column
 //     items with two blocks per wave, so the final round of workgroups is
 //     made of half-length pieces.
 //   * Each group's scale and bias are read once per work unit with coalesced
@@ -63,7 +64,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kGemmThreads / 64;
-constexpr int kColsMax = 512;                     // weight rows (output columns) of a full-width item
+constexpr int kColsMax = kGemmCols;              // weight rows (output columns) of a full-width item
 constexpr int kCBFull = kColsMax / (16 * kWaves); // 16-column MFMA blocks per wave, full-width items
 
 constexpr int kKStep = 128;                       // K per step (4 quarters x 32)
@@ -71,7 +72,8 @@ constexpr int kRowBytes = kKStep * 2;             // one row of one step in LDS 
 constexpr int kBufBytes = kUnitRows * kRowBytes;  // one step of a full unit (24 KiB)
 constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 
-constexpr int kTabGroups = 32;                     // scale/bias groups held at a time (2048 inputs)
+constexpr int kTabGroups = MOE_GEMM_TAB_GROUPS;    // scale/bias groups held at a time
+constexpr int kTabSteps = kTabGroups * 64 / kKStep; // K steps covered by one table fill
 constexpr int kTabStride = kColsMax + 16;          // dwords per group row of the table (padded)
 
 template <int CB>
@@ -211,9 +213,10 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     }
   };
 
-  // Scale/bias table for groups [32 gc, 32 gc + 32): tab[g][c] holds
-  // (fp16 s, fp16 (b + 8 s)) of group g of table column c. Filled with
-  // coalesced loads once per 2048 inputs instead of per step and lane.
+  // Scale/bias table for groups [kTabGroups gc, kTabGroups (gc + 1)):
+  // tab[g][c] holds (fp16 s, fp16 (b + 8 s)) of group g of table column c.
+  // Filled with coalesced loads once per kTabGroups * 64 inputs instead of
+  // per step and lane.
   auto fill_table = [&](int gc) {
     const int g0 = kTabGroups * gc, GC = min(kTabGroups, G - g0);
     if ((G & 7) == 0 && (GC & 7) == 0) {
@@ -397,8 +400,8 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // same number in flight and the compiler's wait counts stay exact.
   auto body = [&](int s, const Stage &cur, Stage &nxt) {
     lds_barrier();
-    if (!WX && s > 0 && s < steps && (s & 15) == 0) {  // next 2048 inputs: next table chunk
-      fill_table(s >> 4);
+    if (!WX && s > 0 && s < steps && s % kTabSteps == 0) {  // next table chunk
+      fill_table(s / kTabSteps);
       lds_barrier();
     }
     const int sn = min(s + 1, steps - 1);
@@ -464,7 +467,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 }
 
 template <int MODE, bool AF16, bool WX>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
   __shared__ uint32_t tab[kTabGroups * kTabStride];
   __shared__ int s_arow[kUnitRows];

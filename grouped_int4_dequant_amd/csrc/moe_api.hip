@@ -22,7 +22,10 @@ constexpr int kMaxRouteTokens = MOE_MAX_CALL_TOKENS;
 constexpr int kMaxTopK = 64;  // one selected expert per lane of the top-k wave
 // Trailing units of the routed work lists that run as half-width items, so
 // the last round of workgroups is made of short pieces.
-constexpr int kNarrowTail = 32;
+#ifndef MOE_GEMM_NARROW_TAIL
+#define MOE_GEMM_NARROW_TAIL 32
+#endif
+constexpr int kNarrowTail = MOE_GEMM_NARROW_TAIL;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -319,7 +322,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   // gate/up projection + SwiGLU: shared expert (implicit units), routed experts
   // (unfused ablation: weights first expanded into the workspace, items of
   // 128 columns of h)
-  const int hcols = opt.unfused ? 128 : 256;
+  const int hcols = opt.unfused ? kGemmCols / 4 : kGemmCols / 2;
   if (opt.unfused) {
     st = hip_status(launch_expand(L->gu_q, L->gu_s, L->gu_b, (int64_t)E * 2 * f, d, wx, s));
     if (st == MOE_OK && fs > 0)
@@ -360,7 +363,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   g1.total_wg = nwg;
   st = hip_status(launch_gemm(g1, kSwiGLU, true, s, nullptr, ev ? ev[3] : nullptr, opt.unfused));
   if (st != MOE_OK) return st;
-  const int ocols = opt.unfused ? 256 : 512;
+  const int ocols = opt.unfused ? kGemmCols / 2 : kGemmCols;
   if (opt.unfused) {
     st = hip_status(launch_expand(L->dn_q, L->dn_s, L->dn_b, (int64_t)E * d, f, wx, s));
     if (st == MOE_OK && fs > 0)
@@ -476,7 +479,7 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row, 
   p.wq_estride = (int64_t)N * (K / 8); p.ws_estride = (int64_t)N * (K / 64);
   p.N = N; p.K = K;
   p.units = block_map; p.num_units = num_blocks; p.implicit_rows = 0;
-  p.nslices = (int)ceil_div(N, 512);
+  p.nslices = (int)ceil_div(N, kGemmCols);
   p.wg_begin = 0;
   p.C = C; p.ldc = ldc;
   g.nprob = 1;
