@@ -9,8 +9,10 @@ grouped GEMM with SwiGLU and the down grouped GEMM with the weighted combine.
 
 Prints one JSON line: tokens/s (value), the roofline of the dominant kernel
 measured with HIP events recorded on the layer's stream inside the timed
-region, the T=1 decode bandwidth, and the CPU oracle timed on a bounded
-sample of the same workload (a baseline, not a target).
+region, the T=1 and T=4 decode bandwidth, the other prefill workloads (the
+512-token layer and the Zipf-skewed 8192-token prompt in 2048-token chunks),
+and the CPU oracle timed on a bounded sample of the same workload (a
+baseline, not a target).
 """
 from __future__ import annotations
 
@@ -37,9 +39,9 @@ METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak
 TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "02b4a7788ca01534fdc29d75da2884ebc30663510fe89ca89a34bb12765d93dc"
-TRAFFIC_BYTES = {"gate_up": (184081.5 * 2.0 + 18432.6) * 1024,
-                 "down_combine": (86167.2 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.5) * 1024}
+TRAFFIC_DIGEST = "861fe082b00379985f0420152ae78d87f7e388d01990d99dced75febae306ce9"
+TRAFFIC_BYTES = {"gate_up": (207925.7 * 2.0 + 18472.0) * 1024,
+                 "down_combine": (85757.7 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.5) * 1024}
 
 
 def sources_digest():
@@ -98,6 +100,9 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB three times "
                          "(a known-size kernel for calibrating hardware byte counters; 0: none)")
+    ap.add_argument("--other-configs", type=int, default=1,
+                    help="also time the 512-token layer and the skewed 8192-token prompt in 2048-token "
+                         "chunks (0: skip)")
     ap.add_argument("--ablations", type=str, default="",
                     help="comma-separated token counts: also time the layer's ablation forms "
                          "(16-row work units; routing built on the host; weights expanded in memory "
@@ -239,6 +244,9 @@ def main():
     out["router"] = bench_router(moe, S, torch, x, sh, args.steps)
     if args.decode_steps > 0:
         out["decode_t1"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events)
+        out["decode_t4"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events, T=4)
+    if args.other_configs:
+        out["other_configs"] = bench_prefill_configs(moe, S, torch, dev, args.steps)
     if args.ablations:
         out["ablations_us"] = bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream,
                                               [int(t) for t in args.ablations.split(",")],
@@ -269,6 +277,57 @@ def bench_router(moe, S, torch, x, sh, steps):
     us = e0.elapsed_time(e1) * 1e3 / steps
     return {"T": T, "d": sh.d, "E": sh.E, "us_per_call": us,
             "tflops": 2.0 * T * sh.d * sh.E / (us * 1e-6) / 1e12}
+
+
+def bench_prefill_configs(moe, S, torch, dev, steps):
+    """The other prefill workloads, each with inputs resident in HBM: the
+    512-token layer (one moe_layer_forward call) and the 8192-token prompt
+    with Zipf-skewed routing (one moe_prefill_chunked call over four
+    2048-token chunks). GPU time per call from events around back-to-back
+    calls after a warm-up; weight bytes count each chunk's touched experts
+    (from the logits) plus the shared expert, read once per chunk."""
+    res = {}
+    for ci in (1, 3):
+        cfg = S.CONFIGS[ci]
+        sh, T, chunk = cfg.shape, cfg.T, cfg.chunk
+        p = S.make_problem(ci)
+        layer = moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, p.layer, device=dev)
+        x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        lg = torch.from_numpy(p.logits).to(dev)
+        y = torch.empty((T, sh.d), dtype=torch.float32, device=dev)
+        ws = moe.alloc_workspace(moe.workspace_bytes(chunk or T, layer), dev)
+        if chunk:
+            def call():
+                moe.prefill_chunked(layer, x, lg, chunk, y=y, ws=ws)
+        else:
+            def call():
+                moe.layer_forward(layer, x, lg, y=y, ws=ws)
+        n = max(1, steps if not chunk else steps // 4)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        c = chunk or T
+        touched = [int(len(np.unique(np.argsort(-p.logits[i:i + c], axis=1, kind="stable")[:, :sh.k])))
+                   for i in range(0, T, c)]
+        wbytes = sum((t + 1) * S.bytes_per_expert(sh) for t in touched)
+        flops = S.useful_flops_per_token(sh) * T
+        res[cfg.name] = {"T": T, "chunk": chunk, "calls": n, "us_per_call": us,
+                         "tokens_per_s": T / (us * 1e-6),
+                         "useful_tflops": flops / (us * 1e-6) / 1e12,
+                         "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
+                         "touched_experts_per_chunk": touched, "weight_bytes": wbytes,
+                         "weight_gbps": wbytes / (us * 1e-6) / 1e9,
+                         "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del layer, x, lg, y, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream, tokens, steps, warmup):
@@ -302,8 +361,8 @@ def bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream, tokens, ste
     return res
 
 
-def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
-    """T=1 steps with fresh logits and x, rotating over 4 device copies of the
+def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events, T=1):
+    """Decode steps of T tokens (1 or 4) with fresh logits and x, rotating over 4 device copies of the
     weights (about 1.8 GB, larger than the last-level cache) so repeated
     experts are not served from cache. Bytes per step are exact: the packed
     codes, scales and biases of the distinct experts touched plus the shared
@@ -315,17 +374,17 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
     The replay's last output is checked against the eager one."""
     cfg = S.CONFIGS[4]
     sh = cfg.shape
-    steps = list(S.decode_steps(1, steps=nsteps + 20))
+    steps = list(S.decode_steps(T, steps=nsteps + 20))
     layers = [moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, steps[0].layer, device=dev)
               for _ in range(4)]
     xs = [torch.from_numpy(s.x.view(np.int16)).view(torch.bfloat16).to(dev) for s in steps]
     lgs = [torch.from_numpy(s.logits).to(dev) for s in steps]
-    ys = [torch.empty((1, sh.d), dtype=torch.float32, device=dev) for _ in steps]
-    ws = moe.alloc_workspace(moe.workspace_bytes(1, layers[0]), dev)
+    ys = [torch.empty((T, sh.d), dtype=torch.float32, device=dev) for _ in steps]
+    ws = moe.alloc_workspace(moe.workspace_bytes(T, layers[0]), dev)
     per_expert = S.bytes_per_expert(sh)
     nbytes = []
     for s in steps:
-        touched = len(np.unique(np.argsort(-s.logits[0], kind="stable")[:sh.k]))
+        touched = len(np.unique(np.argsort(-s.logits, axis=1, kind="stable")[:, :sh.k]))
         nbytes.append((touched + 1) * per_expert)
 
     def run(i):
@@ -366,7 +425,7 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events):
     gpu = g0.elapsed_time(g1) * 1e-3 / (reps * nsteps)
     same = bool(torch.equal(ys[19 + nsteps], y_eager))
     b = float(np.mean(nbytes[20:]))
-    return {"T": 1, "steps": nsteps, "bytes_per_step": b,
+    return {"T": T, "steps": nsteps, "bytes_per_step": b,
             "gpu_us_per_step": gpu * 1e6, "eager_gpu_us_per_step": eager_gpu * 1e6,
             "wall_us_per_step": wall * 1e6, "graph_replay_matches_eager": same,
             "gbps_gpu": b / gpu / 1e9, "gbps_eager": b / eager_gpu / 1e9,

@@ -8,9 +8,9 @@
 //
 //   gate/up  one workgroup per (distinct routed expert or the shared expert,
 //            16 columns of h), one wave per 512 inputs.
-//            Every workgroup first repeats the top-k for the call's tokens
-//            (a wave max over order-preserving 64-bit keys, as in the routing
-//            kernel) and ranks the distinct experts with a bitmap, so no
+//            Every workgroup first repeats the top-k for the call's tokens,
+//            one token per wave (a wave max over order-preserving 64-bit
+//            keys, as in the routing kernel), and ranks the distinct experts with a bitmap, so no
 //            routing kernel runs before it. The waves' partial sums meet in
 //            LDS; SwiGLU gives fp32 h per (token, slot).
 //   down     one workgroup per (token, 16 output columns), one wave per slot
@@ -73,16 +73,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   const int u = blockIdx.x / chunks, hc = blockIdx.x - u * chunks;
   const bool shared = u == P;
 
-  // ---- the call's activations (bf16 [T][d]) are requested first, for LDS;
-  // their latency hides behind the routing
+  // ---- the call's activations (bf16 [T][d]) go to LDS. One token: each
+  // thread's chunk is requested first, so its latency hides behind the
+  // routing. Several tokens: the chunks are copied after the weight requests
+  // below, so none is held in registers across the top-k.
   extern __shared__ uint4 s_x[];  // [T * d / 8]
-  // T * d / 8 chunks over 64 * d / 512 threads: T chunks per thread, all
-  // requested unconditionally (past T: the last chunk again), so none waits
-  // on another
-  constexpr int kXPer = ONE ? 1 : kDecodeMaxT;
-  uint4 xr_[kXPer];
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i) xr_[i] = reinterpret_cast<const uint4 *>(a.x)[tid + min(i, T - 1) * nthreads];
+  uint4 xr0 = make_uint4(0u, 0u, 0u, 0u);
+  if (ONE) xr0 = reinterpret_cast<const uint4 *>(a.x)[tid];
 
   // ---- routing, repeated by every workgroup of a routed expert
   if (!shared && ONE) {
@@ -106,17 +103,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   } else if (!shared) {
   for (int i = tid; i < nwords; i += nthreads) s_bits[i] = 0u;
   if (tid < kDecodeMaxPairs) s_umask[tid] = 0u;
-  if (wave == 0) {
-    for (int t = 0; t < T; ++t) {
-      int id;
-      float g;
-      topk_wave<VPL>(a.logits + (int64_t)t * E, E, k, lane, id, g);
-      if (lane < k) {
-        s_ids[t * k + lane] = id;
-        if (blockIdx.x == 0) {
-          a.ids[t * k + lane] = id;
-          a.gates[t * k + lane] = g;
-        }
+  // one token per wave, so the tokens' top-k run side by side
+  const int nw = nthreads / 64;
+  for (int t = wave; t < T; t += nw) {
+    int id;
+    float g;
+    topk_wave<VPL>(a.logits + (int64_t)t * E, E, k, lane, id, g);
+    if (lane < k) {
+      s_ids[t * k + lane] = id;
+      if (blockIdx.x == 0) {
+        a.ids[t * k + lane] = id;
+        a.gates[t * k + lane] = g;
       }
     }
   }
@@ -175,9 +172,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   }
   // activations into LDS (their loads were issued first), then row c16's
   // fragments (a token of the mask, else the first token's, zeroed at use)
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i)
-    if (i < T) s_x[tid + i * nthreads] = xr_[i];  // LDS stores only: no load depends on them
+  if (ONE) {
+    s_x[tid] = xr0;
+  } else {
+    // T chunks per thread, requested behind the weights: waiting for them
+    // also waits for the weights, which the MFMAs need next anyway
+    const uint4 *xg = reinterpret_cast<const uint4 *>(a.x);
+    for (int i = tid; i < T * nthreads; i += nthreads) s_x[i] = xg[i];
+  }
   __syncthreads();
   const bool has_row = c16 < nrows;
   const int tok = nth_bit(mask, has_row ? c16 : 0);
