@@ -231,6 +231,24 @@ def test_layer_full_config(moe, index):
     check_output(y[tok], y_ref, f"config {index} sampled")
 
 
+@pytest.mark.parametrize("index", [1, 2])
+def test_layer_bit_reproducible(moe, index):
+    """Repeated calls on the same inputs give the same y bit for bit (every
+    reduction has a fixed order; no atomics), whatever else ran between them."""
+    p = S.make_problem(index)
+    say(f"layer determinism config {index} T={p.T} x12")
+    layer, x, lg = upload(p, moe)
+    ws = moe.alloc_workspace(moe.workspace_bytes(p.T, layer))
+    first = moe.layer_forward(layer, x, lg, ws=ws).clone()
+    for r in range(12):
+        y = torch.empty_like(first)
+        for _ in range(1 + (7 * r) % 5):
+            moe.layer_forward(layer, x, lg, y=y, ws=ws)
+        torch.cuda.synchronize()
+        diff = (y != first).sum().item()
+        assert diff == 0, f"repeat {r}: {diff} output elements differ"
+
+
 def test_chunked_config3(moe):
     p = S.make_problem(3)
     say("config 3: T=8192 in 2048-token chunks (skewed)")
