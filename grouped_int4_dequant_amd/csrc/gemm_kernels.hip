@@ -384,7 +384,12 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
         if (j + 1 < 4 && cb > 0) bq[cb - 1] = rebuild(j + 1, cb - 1);
 #pragma unroll
         for (int rb = 0; rb < kMaxRB; ++rb) {
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb], bq[cb], acc[rb][cb], 0, 0, 0);
+          // down projection: weights as the first operand, so a lane's four
+          // accumulators are four adjacent output columns of one row
+          if constexpr (MODE == kStoreH)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[cb], af[rb], acc[rb][cb], 0, 0, 0);
+          else
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb], bq[cb], acc[rb][cb], 0, 0, 0);
           if (cb == kCB - 1 && j + 1 < 4) af[rb] = read_a(j + 1, rb);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -421,29 +426,95 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     body(s + 1, b1, b0);
   }
 
-  if (!active) return;
   // ------------------------------------------------------------- epilogue
-  // accumulator element i of lane (c16, kq) in block (rb, cb) is row
-  // 16*rb + 4*kq + i, column 16*cb + c16 of the wave's tile
-  if (MODE == kSwiGLU) {
-    const int ng = U.slice * (kCols / 2) + wave * 8 * kCB;
+  if constexpr (MODE == kSwiGLU) {
+    // Gate/up projection: h = silu(gate) * up goes out through LDS in whole
+    // 16-byte stores, one 8-run of the permuted-run layout each. The tile
+    // (up to 96 rows x kCols/2 h columns, 256-byte rows) sits in the free
+    // activation buffers with its 16-byte chunks XOR-swizzled by row (chunk
+    // c of row r at c ^ (r & 15)). Accumulator element i of lane (c16, kq)
+    // in block (rb, cb) is row 16*rb + 4*kq + i, h column 16*cb + c16 of the
+    // wave's gate (cb < kHalf) or up (cb >= kHalf) half. Idle waves take
+    // part in the barriers.
+    constexpr int kHCols = kCols / 2;
+    lds_barrier();
+    if (active) {
 #pragma unroll
-    for (int rb = 0; rb < kMaxRB; ++rb) {
+      for (int rb = 0; rb < kMaxRB; ++rb) {
 #pragma unroll
-      for (int cb = 0; cb < kHalf; ++cb) {
-        const int col = perm_col(ng + 16 * cb + c16);
+        for (int cb = 0; cb < kHalf; ++cb) {
+          const int lc = perm_col(wave * 8 * kCB + 16 * cb + c16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rb + 4 * kq + i;
-          if (r < nr) {
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + 4 * kq + i;
             const float g = acc[rb][cb][i], u = acc[rb][cb + kHalf][i];
             const float h = g / (1.f + __expf(-g)) * u;
-            P.H[(int64_t)(U.r0 + r) * P.ldh + col] = f32_to_f16_bits(h);
+            *reinterpret_cast<uint16_t *>(lds + r * 256 + 16 * ((lc >> 3) ^ (r & 15)) + 2 * (lc & 7)) =
+                f32_to_f16_bits(h);
           }
         }
       }
     }
-  } else {
+    lds_barrier();
+    constexpr int kRowLanes = kHCols / 8;
+    constexpr int kRowsPerPass = kGemmThreads / kRowLanes;
+    const int j = tid % kRowLanes, n = U.slice * kHCols + 8 * j;
+    for (int r = tid / kRowLanes; r < nr; r += kRowsPerPass) {
+      if (n < (N >> 1)) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(lds + r * 256 + 16 * (j ^ (r & 15)));
+        *reinterpret_cast<uint4 *>(P.H + (int64_t)(U.r0 + r) * P.ldh + n) = v;
+      }
+    }
+    return;
+  }
+
+  if constexpr (MODE == kStoreH) {
+    // Down projection: the tile leaves through LDS so every row goes out as
+    // whole 16-byte lane stores (32 lanes per 512-byte row of 256 columns)
+    // instead of 2-byte ones. The activation buffers (2 x 24 KiB) are free
+    // once every wave has finished its last step: they hold the item's
+    // fp16 tile, 96 rows x 512 bytes, in 8-byte units XOR-swizzled by row
+    // (unit u of row r at u ^ (r & 15)) so the writes of one instruction
+    // spread over all banks. Accumulator element i of lane (c16, kq) in
+    // block (rb, cb) is row 16*rb + c16, column 16*cb + 4*kq + i of the
+    // wave's tile. Idle waves take part in the barriers.
+    constexpr int kUnits = kCols / 4;  // 8-byte units of one tile row
+    static_assert(kUnitRows * 512 <= 2 * kBufBytes, "output tile fits the activation buffers");
+    lds_barrier();
+    if (active) {
+#pragma unroll
+      for (int rb = 0; rb < kMaxRB; ++rb) {
+        const int r = 16 * rb + c16;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) {
+          const int u = wave * 4 * kCB + 4 * cb + kq;
+          const uint32_t lo = f32_to_f16_bits(acc[rb][cb][0]) | ((uint32_t)f32_to_f16_bits(acc[rb][cb][1]) << 16);
+          const uint32_t hi = f32_to_f16_bits(acc[rb][cb][2]) | ((uint32_t)f32_to_f16_bits(acc[rb][cb][3]) << 16);
+          *reinterpret_cast<uint2 *>(lds + r * 512 + 8 * (u ^ (r & 15))) = make_uint2(lo, hi);
+        }
+      }
+    }
+    lds_barrier();
+    // 16-byte chunk j (units 2j, 2j+1) of row r; kUnits / 2 lanes per row
+    constexpr int kRowLanes = kUnits / 2;
+    constexpr int kRowsPerPass = kGemmThreads / kRowLanes;
+    const int j = tid % kRowLanes, n = U.slice * kCols + 8 * j;
+    for (int r = tid / kRowLanes; r < nr; r += kRowsPerPass) {
+      if (n < N) {
+        const uint8_t *src = lds + r * 512;
+        const uint2 a = *reinterpret_cast<const uint2 *>(src + 8 * ((2 * j) ^ (r & 15)));
+        const uint2 b = *reinterpret_cast<const uint2 *>(src + 8 * ((2 * j + 1) ^ (r & 15)));
+        *reinterpret_cast<uint4 *>(P.H + (int64_t)(U.r0 + r) * P.ldh + n) = make_uint4(a.x, a.y, b.x, b.y);
+      }
+    }
+    return;
+  }
+
+  // stand-alone grouped GEMM: fp32 C stored directly (accumulator element i
+  // of lane (c16, kq) in block (rb, cb) is row 16*rb + 4*kq + i, column
+  // 16*cb + c16 of the wave's tile)
+  if (!active) return;
+  {
     const int n0 = U.slice * kCols + wave * 16 * kCB;
 #pragma unroll
     for (int rb = 0; rb < kMaxRB; ++rb) {
@@ -451,15 +522,9 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * kq + i;
         if (r < nr) {
-          if (MODE == kStoreH) {
-            uint16_t *orow = P.H + (int64_t)(U.r0 + r) * P.ldh + n0 + c16;
+          float *crow = P.C + (int64_t)(U.r0 + r) * P.ldc + n0 + c16;
 #pragma unroll
-            for (int cb = 0; cb < kCB; ++cb) orow[16 * cb] = f32_to_f16_bits(acc[rb][cb][i]);
-          } else {
-            float *crow = P.C + (int64_t)(U.r0 + r) * P.ldc + n0 + c16;
-#pragma unroll
-            for (int cb = 0; cb < kCB; ++cb) crow[16 * cb] = acc[rb][cb][i];
-          }
+          for (int cb = 0; cb < kCB; ++cb) crow[16 * cb] = acc[rb][cb][i];
         }
       }
     }
