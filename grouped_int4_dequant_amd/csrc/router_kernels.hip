@@ -5,11 +5,13 @@
 // x and W_r are bf16; products are exact in fp32 and accumulate in fp32 with
 // v_mfma_f32_16x16x32_bf16 in a fixed order (32 inputs per MFMA, ascending),
 // so repeated calls give identical logits. A workgroup of four waves covers
-// 32 tokens x 64 experts; a wave owns 16 experts and both 16-row blocks, and
-// reads its operands straight from memory (each 16-byte fragment is one
-// token's or one expert's eight consecutive inputs), requesting the next
-// four 32-input steps before computing the current four.
-//
+// 32 tokens x 64 experts; a wave owns 16 experts and both 16-row blocks.
+// The token rows are shared by the four waves, so they pass through LDS once
+// per workgroup in chunks of 256 inputs (double buffered, 16-byte units
+// XOR-swizzled by row so the 16 rows read by one MFMA operand fetch hit
+// distinct banks); each wave reads its experts' weights straight from
+// memory, requesting the next chunk's before computing the current one.
+
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
 //            for Qwen3.6-35B-A3B on Apple Silicon" (insight.aitobox.com)
@@ -24,50 +26,84 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRouterRows = 32;     // tokens per workgroup
 constexpr int kRouterExperts = 64;  // experts per workgroup (16 per wave)
-constexpr int kGroupSteps = 4;      // 32-input steps requested together
+constexpr int kChunkSteps = 8;      // 32-input steps per LDS chunk (256 inputs)
+constexpr int kRowBytes = kChunkSteps * 64;  // one token row of a chunk (bf16)
 
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kRouterRows * kRowBytes];  // 2 x 16 KiB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * kRouterRows;
   const int e = blockIdx.y * kRouterExperts + wave * 16 + c16;
-  // rows and experts past the end read the last valid one (never stored)
+  // experts past the end read the last valid one (never stored)
   const int ec = min(e, a.E - 1);
-  const int tr0 = min(t0 + c16, a.T - 1), tr1 = min(t0 + 16 + c16, a.T - 1);
-  const uint4 *xa = reinterpret_cast<const uint4 *>(a.x + (int64_t)tr0 * a.d) + kq;
-  const uint4 *xb = reinterpret_cast<const uint4 *>(a.x + (int64_t)tr1 * a.d) + kq;
   const uint4 *wr = reinterpret_cast<const uint4 *>(a.w + (int64_t)ec * a.d) + kq;
-  const int steps = a.d / 32;  // 16-byte chunks: 4 per step; this lane's is chunk kq
+  const int steps = a.d / 32;                             // this lane's 16-byte chunk of step s is 4 s + kq
+  const int nchunks = (steps + kChunkSteps - 1) / kChunkSteps;
+
+  // token-row staging: unit u = tid + 256 i of a chunk is row u / 32, 16-byte
+  // column u % 32 (rows past T repeat the last token; columns past d are not
+  // read back)
+  static_assert(kRouterRows * (kRowBytes / 16) == 4 * 256, "four 16-byte units per thread and chunk");
+  auto x_src = [&](int c, int i) {
+    const int u = tid + 256 * i, r = u >> 5, j = u & 31;
+    const int tr = min(t0 + r, a.T - 1);
+    const int col = min(c * kChunkSteps * 32 + 8 * j, a.d - 8);  // clamped, never read back past d
+    return reinterpret_cast<const uint4 *>(a.x + (int64_t)tr * a.d + col);
+  };
+  auto x_dst = [&](int buf, int i) {
+    const int u = tid + 256 * i, r = u >> 5, j = u & 31;
+    return reinterpret_cast<uint4 *>(&s_x[buf][r * kRowBytes + 16 * (j ^ (r & 15))]);
+  };
+  uint4 x0, x1, x2, x3;  // this thread's four units of the next chunk
+  auto load_x = [&](int c) {
+    x0 = *x_src(c, 0);
+    x1 = *x_src(c, 1);
+    x2 = *x_src(c, 2);
+    x3 = *x_src(c, 3);
+  };
+  auto store_x = [&](int buf) {
+    *x_dst(buf, 0) = x0;
+    *x_dst(buf, 1) = x1;
+    *x_dst(buf, 2) = x2;
+    *x_dst(buf, 3) = x3;
+  };
+  typedef uint4 WChunk[kChunkSteps];
+  auto load_w = [&](WChunk &cw, int c) {
+#pragma unroll
+    for (int u = 0; u < kChunkSteps; ++u) cw[u] = wr[4 * min(c * kChunkSteps + u, steps - 1)];
+  };
 
   f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = f4{0.f, 0.f, 0.f, 0.f};
-  uint4 ca[kGroupSteps], cb[kGroupSteps], cw[kGroupSteps];
-  auto load = [&](int s0) {
+  // One chunk: the barrier publishes chunk c in LDS and frees the other
+  // buffer; chunk c+1's rows and weights are requested (the last chunk
+  // requests itself again), chunk c is computed, then c+1's rows go to LDS.
+  auto body = [&](int c, const WChunk &w, WChunk &wn) {
+    __syncthreads();
+    const int cn = min(c + 1, nchunks - 1);
+    load_x(cn);
+    load_w(wn, cn);
+    const uint8_t *xb = s_x[c & 1];
 #pragma unroll
-    for (int u = 0; u < kGroupSteps; ++u) {
-      const int s = min(s0 + u, steps - 1);
-      ca[u] = xa[4 * s];
-      cb[u] = xb[4 * s];
-      cw[u] = wr[4 * s];
-    }
-  };
-  load(0);
-  for (int s0 = 0; s0 < steps; s0 += kGroupSteps) {
-    uint4 na[kGroupSteps], nb[kGroupSteps], nw[kGroupSteps];
-#pragma unroll
-    for (int u = 0; u < kGroupSteps; ++u) {
-      na[u] = ca[u];
-      nb[u] = cb[u];
-      nw[u] = cw[u];
-    }
-    load(s0 + kGroupSteps);  // next group (clamped at the end: reloads the last step)
-#pragma unroll
-    for (int u = 0; u < kGroupSteps; ++u) {
-      if (s0 + u < steps) {
-        const bf8 w = __builtin_bit_cast(bf8, nw[u]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, na[u]), w, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, nb[u]), w, acc1, 0, 0, 0);
+    for (int u = 0; u < kChunkSteps; ++u) {
+      if (c * kChunkSteps + u < steps) {
+        const int j = 4 * u + kq;
+        const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
+        const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
+        const bf8 wv = __builtin_bit_cast(bf8, w[u]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), wv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), wv, acc1, 0, 0, 0);
       }
     }
+    store_x((c + 1) & 1);
+  };
+  WChunk w0, w1;
+  load_x(0);
+  load_w(w0, 0);
+  store_x(0);
+  for (int c = 0; c < nchunks; c += 2) {
+    body(c, w0, w1);
+    if (c + 1 < nchunks) body(c + 1, w1, w0);
   }
   // element i of lane (c16, kq): token row 4 kq + i of the block, expert c16
   if (e < a.E) {
