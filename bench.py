@@ -39,7 +39,7 @@ METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak
 TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "892111074a49f1dde6ef9e74747b006a2eacc5dd66684e2ae4b09e5bd6239d6d"
+TRAFFIC_DIGEST = "c190846f395621910a102b3468407bba2b6b43078d4aa34aabe079d27221ae33"
 TRAFFIC_BYTES = {"gate_up": (208242.8 * 2.0 + 18432.0) * 1024,
                  "down_combine": (85730.9 * 2.0 + 73728.0 + 37144.5 * 2.0 + 16384.8) * 1024}
 

@@ -75,6 +75,10 @@ constexpr int kSlabRows = 1024 / kRowBytes;       // rows per 1 KiB wave store
 constexpr int kTabGroups = MOE_GEMM_TAB_GROUPS;    // scale/bias groups held at a time
 constexpr int kTabSteps = kTabGroups * 64 / kKStep; // K steps covered by one table fill
 constexpr int kTabStride = kColsMax + 16;          // dwords per group row of the table (padded)
+static_assert(kCBFull == 4, "a wave owns four 16-column MFMA blocks of a full-width item");
+static_assert((kTabGroups & (kTabGroups - 1)) == 0 && kTabGroups * 64 % kKStep == 0, "table of whole steps");
+static_assert(MOE_GEMM_WGS_PER_CU * (2 * kBufBytes + kTabGroups * kTabStride * 4 + kUnitRows * 4) <= 160 * 1024,
+              "the resident workgroups' LDS fits one CU");
 
 template <int CB>
 struct BStage {

@@ -16,16 +16,13 @@ constexpr int kUnitRows = 96;      // max rows of one GEMM work unit (three 32-r
 constexpr int kSubChunk = 64;      // tokens per routing bitmask (one wave's lanes)
 constexpr int kThreads = 256;      // threads per workgroup of the routing and combine kernels
 // Grouped-GEMM workgroup shape (compile-time; the defaults are the measured
-// best): waves per workgroup, weight rows (output columns) of a full-width
-// item, scale/bias groups held in the LDS table at a time, and workgroups
-// resident per CU. Two 4-wave workgroups per CU (one wave of each per SIMD,
+// best): waves per workgroup (each owns 64 weight rows, i.e. output
+// columns, of a full-width item), scale/bias groups held in the LDS table at
+// a time, and workgroups resident per CU. Two 4-wave workgroups per CU (one wave of each per SIMD,
 // about 65 KiB of LDS each) keep the matrix pipes busy while the other
 // workgroup waits at its barrier or runs its prologue or epilogue.
 #ifndef MOE_GEMM_WAVES
 #define MOE_GEMM_WAVES 4
-#endif
-#ifndef MOE_GEMM_COLS
-#define MOE_GEMM_COLS 256
 #endif
 #ifndef MOE_GEMM_TAB_GROUPS
 #define MOE_GEMM_TAB_GROUPS 16
@@ -34,7 +31,7 @@ constexpr int kThreads = 256;      // threads per workgroup of the routing and c
 #define MOE_GEMM_WGS_PER_CU 2
 #endif
 constexpr int kGemmThreads = 64 * MOE_GEMM_WAVES;  // threads per workgroup of the grouped GEMM
-constexpr int kGemmCols = MOE_GEMM_COLS;           // weight rows of a full-width GEMM item
+constexpr int kGemmCols = 64 * MOE_GEMM_WAVES;     // weight rows of a full-width GEMM item (64 per wave)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
