@@ -269,11 +269,16 @@ def test_chunked_config3(moe):
 
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_config4(moe, T):
-    say(f"config 4 decode T={T}: 60 steps")
+    """Config 4's parity schedule: routing checked on every one of the 1000
+    seeded steps, outputs on steps 0, 999 and every 20th step."""
+    nsteps = S.CONFIGS[4].steps
+    say(f"config 4 decode T={T}: {nsteps} steps")
     cache = {}
     layer = None
     ys, refs = [], []
-    for step, p in enumerate(S.decode_steps(T, steps=60)):
+    for step, p in enumerate(S.decode_steps(T)):
+        if step % 200 == 0:
+            say(f"  step {step}")
         if layer is None:
             layer, _, _ = upload(p, moe)
         x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
@@ -282,7 +287,7 @@ def test_decode_config4(moe, T):
         y = moe.layer_forward(layer, x, lg, routing=routing)
         torch.cuda.synchronize()
         check_routing(routing, O.route(p.logits, p.shape.k), T, p.shape.k)
-        if step % 20 == 0 or step == 59:
+        if step % 20 == 0 or step == nsteps - 1:
             ys.append(y.cpu().numpy())
             refs.append(O.moe_forward(p.layer, p.x, p.logits, p.shape.k, weight_cache=cache))
     check_output(np.concatenate(ys), np.concatenate(refs), f"decode T={T}")
