@@ -170,8 +170,8 @@ EDGE_SHAPES = [
     (300, 512, 320, 12, 3, 192),
     (50, 2560, 192, 4, 2, 64),      # K = 2560: scale/bias table refilled every 1024 inputs, last chunk partial
     (40, 448, 576, 5, 2, 0),        # 7 groups along d: scalar table fill
-    (50, 1024, 192, 4, 2, 0),       # 4 units (not a multiple of 8), down in four 256-column slices
-    (50, 768, 192, 4, 2, 64),       # all gate/up units half-width; down in three 256-column slices
+    (50, 1024, 192, 4, 2, 0),       # 4 units (not a multiple of 8), all half-width: down in eight 128-column slices
+    (50, 768, 192, 4, 2, 64),       # all units half-width; down in six 128-column slices over d = 768
     (256, 1024, 256, 64, 4, 256),   # 64 units: 32 full-width + 32 half-width (128-column) units
     # persistent streaming GEMM (K a multiple of 512, at most 2048)
     (40, 512, 512, 8, 2, 512),      # four steps per item, shared rows after routed rows
