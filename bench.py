@@ -95,7 +95,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed layer calls for this long before the warm-up steps (clock ramp-up)")
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-steps", type=int, default=1000,
+                    help="decode steps per token count (the 1000-step decode workload)")
     ap.add_argument("--cpu-tokens", type=int, default=2048, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB three times "
