@@ -39,7 +39,7 @@ METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak
 TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "b922eeafc924a71cc49164657215ddd7a4dc6941bcda815377c446ea37a5df29"
+TRAFFIC_DIGEST = "b62d8d2ead83f75c16af3f32b3338e3fbb65219fa70354e8787e4636ee83ee01"
 TRAFFIC_BYTES = {"gate_up": (208487.5 * 2.0 + 18432.0) * 1024,
                  "down_combine": (85645.3 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.9) * 1024}
 

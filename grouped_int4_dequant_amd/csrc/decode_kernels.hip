@@ -12,11 +12,15 @@
 //            one token per wave (a wave max over order-preserving 64-bit
 //            keys, as in the routing kernel), and ranks the distinct experts with a bitmap, so no
 //            routing kernel runs before it. The waves' partial sums meet in
-//            LDS; SwiGLU gives fp32 h per (token, slot).
-//   down     one workgroup per (token, 16 output columns), one wave per slot
-//            (the k routed experts and the shared expert), 512 inputs each. The partial
+//            LDS; SwiGLU gives h per (token, slot), stored as fp16.
+//   down     one workgroup per (token, 8 output columns), one wave per slot
+//            (the k routed experts and the shared expert), 512 inputs each. A
+//            wave's 16x16 MFMA tile holds its 8 columns twice, over the first
+//            and the second 256 inputs, against tile rows that alternate
+//            between h's two halves, so the wave runs 8 MFMAs and needs no
+//            zeroing. h arrives as fp16 in the MFMA operand order. The partial
 //            projections meet in LDS and are combined in slot order with the
-//            gates: y = sum_j g_j o_j + o_shared, fp32, with no atomics.
+//            gates: y = sum_j g_j (o_j' + o_j'') + o_shared, fp32, no atomics.
 //
 // Weights are rebuilt from the 4-bit codes exactly as in the prefill GEMM
 // (rebuild_device.h) and multiplied with v_mfma_f32_16x16x32_f16; the rows
@@ -55,6 +59,18 @@ __device__ __forceinline__ uint32_t group_consts(const u4v &sw, const u4v &bw, i
   return rb_pack_scale_bias((sw[s] >> sh) & 0xFFFFu, (bw[s] >> sh) & 0xFFFFu);
 }
 
+// Eight bf16 activations -> fp16 in the rebuild order (as one MFMA operand).
+__device__ __forceinline__ uint4 x_chunk_h8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float xf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xf[2 * i] = __uint_as_float(w[i] << 16);
+    xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(uint4, rb_perm8(xf));
+}
+
 // ONE: calls of one token (T == 1), whose k picks are the distinct experts.
 template <int VPL, bool ONE>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a) {
@@ -62,6 +78,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   __shared__ uint32_t s_bits[MOE_MAX_EXPERTS / 32];
   __shared__ int s_uexp[kDecodeMaxPairs];
   __shared__ uint32_t s_umask[kDecodeMaxPairs];
+  __shared__ int8_t s_uslot[kDecodeMaxPairs][kDecodeMaxT];  // slot of token t's pick of distinct expert u
   __shared__ int s_U;
   __shared__ float s_red[kMaxWaves][2][256];
 
@@ -126,6 +143,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     int rank = __popc(s_bits[wi] & ((1u << (e & 31)) - 1u));
     for (int q = 0; q < wi; ++q) rank += __popc(s_bits[q]);
     s_uexp[rank] = e;
+    s_uslot[rank][tid / k] = (int8_t)(tid % k);
     atomicOr(&s_umask[rank], 1u << (tid / k));
   }
   if (tid == 0) {
@@ -170,19 +188,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     sw[cb] = *reinterpret_cast<const u4v *>(wsc + (int64_t)row[cb] * G + kbase / 64);
     bw[cb] = *reinterpret_cast<const u4v *>(wbi + (int64_t)row[cb] * G + kbase / 64);
   }
-  // activations into LDS (their loads were issued first), then row c16's
-  // fragments (a token of the mask, else the first token's, zeroed at use)
+  // activations into LDS as fp16 in the rebuild order (their loads were
+  // issued first), converted once per workgroup; then row c16's fragments:
+  // a token of the mask, else the first one again (a row never read)
   if (ONE) {
-    s_x[tid] = xr0;
+    s_x[tid] = x_chunk_h8(xr0);
   } else {
     // T chunks per thread, requested behind the weights: waiting for them
     // also waits for the weights, which the MFMAs need next anyway
     const uint4 *xg = reinterpret_cast<const uint4 *>(a.x);
-    for (int i = tid; i < T * nthreads; i += nthreads) s_x[i] = xg[i];
+    for (int i = tid; i < T * nthreads; i += nthreads) s_x[i] = x_chunk_h8(xg[i]);
   }
   __syncthreads();
-  const bool has_row = c16 < nrows;
-  const int tok = nth_bit(mask, has_row ? c16 : 0);
+  const int tok = nth_bit(mask, c16 < nrows ? c16 : 0);
   const uint4 *xl = s_x + ((int64_t)tok * d + kbase + 32 * kq) / 8;
   u4v xv[kSteps][4];
 #pragma unroll
@@ -203,14 +221,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     for (int cb = 0; cb < 2; ++cb) sc[cb] = group_consts(sw[cb], bw[cb], s, kq >> 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float xf[8];
-      const u4v w = has_row ? xv[s][j] : u4v{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xf[2 * i] = __uint_as_float(w[i] << 16);
-        xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      const rb_h8 af = rb_perm8(xf);
+      const rb_h8 af = __builtin_bit_cast(rb_h8, xv[s][j]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, rb_rebuild(code[cb][s][j], sc[cb], kc), acc[cb], 0,
@@ -235,11 +246,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
           up += s_red[w][1][4 * lane + i];
         }
         const int t = nth_bit(mask, r);
-        int slot = k;
-        if (!shared)
-          for (int j = 0; j < k; ++j)
-            if (s_ids[t * k + j] == e) slot = j;
-        a.h[((int64_t)t * (k + 1) + slot) * a.fmax + 16 * hc + c16] = g / (1.f + __expf(-g)) * up;
+        // one token: distinct expert u is slot u
+        const int slot = shared ? k : ONE ? u : s_uslot[u][t];
+        // fp16, each 8 columns in the rebuild order, as the down MFMAs take it
+        const int n = 16 * hc + c16;
+        a.h[((int64_t)t * (k + 1) + slot) * a.fmax + (n & ~7) + 2 * (n & 3) + ((n >> 2) & 1)] =
+            __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + __expf(-g)) * up));
       }
     }
   }
@@ -248,77 +260,69 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
 __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeArgs a) {
   __shared__ float s_part[kDecodeMaxSlots][16];
   __shared__ float s_gate[kDecodeMaxSlots];
-  __shared__ f4 s_h[kDecodeMaxSlots * kSpan / 4];  // this token's h, every slot
   const int tid = threadIdx.x, lane = tid & 63, j = tid >> 6;  // wave j: slot j (j == k: shared)
-  const int k = a.k, d = a.d, chunks = d / 16;
-  const int t = blockIdx.x / chunks, cc = blockIdx.x - t * chunks;
+  const int k = a.k, d = a.d, blocks = d / 8;
+  const int t = blockIdx.x / blocks, cc = blockIdx.x - t * blocks;
   const int c16 = lane & 15, kq = lane >> 4;
   const bool shared = j == k;
-  const int fe = shared ? a.f_sh : a.f;
+  const bool live = !shared || a.f_sh > 0;  // a shared wave without a shared expert adds zero
 
-  // Requests, all before any use: this slot's expert and gate, then the
-  // token's h rows ((k + 1) x 512 fp32: two 16-byte chunks per thread),
-  // then the slot's weights (which need the expert).
+  // Requests, all unconditional so no wait covers more than it needs: the
+  // slot's pick and gate, the slot's h, then its weights (which need the
+  // pick). A dead shared wave reads routed expert 0 and is zeroed at the end.
   const int jr = shared ? 0 : j;
   const int e_slot = a.ids[t * k + jr];
   const float g_slot = a.gates[t * k + jr];
-  const f4 *hsrc = reinterpret_cast<const f4 *>(a.h + (int64_t)t * (k + 1) * a.fmax);
-  const f4 h0 = hsrc[tid], h1 = hsrc[tid + 64 * (k + 1)];
-
-  const int e = shared ? 0 : e_slot;
-  const uint32_t *wq = shared ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
-  const uint16_t *wsc = shared ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
-  const uint16_t *wbi = shared ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
-  const int n = 16 * cc + c16;
-  u4v code[kSteps], sw, bw;
-  if (fe > 0) {  // fe == kSpan
-    const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + 4 * kq;
+  // A operand: tile row r holds h's half r & 1 (inputs 256 (r & 1) ...), 8
+  // fp16 per lane and MFMA, already in the rebuild order
+  const uint4 *hs = reinterpret_cast<const uint4 *>(a.h + ((int64_t)t * (k + 1) + j) * a.fmax +
+                                                    (kSpan / 2) * (c16 & 1) + 32 * kq);
+  u4v hv[kSteps / 2][4];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) code[s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
-    sw = *reinterpret_cast<const u4v *>(wsc + (int64_t)n * (kSpan / 64));
-    bw = *reinterpret_cast<const u4v *>(wbi + (int64_t)n * (kSpan / 64));
-  }
-  s_h[tid] = h0;
-  s_h[tid + 64 * (k + 1)] = h1;
-  __syncthreads();
-
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  if (fe > 0) {
-    // activations: row 0 of the tile is this token's h for slot j (lanes
-    // c16 == 0); the other rows are zero
-    const f4 *hr = s_h + (j * kSpan + 32 * kq) / 4;
-    rb_h8 hv[kSteps][4];
+  for (int s = 0; s < kSteps / 2; ++s)
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 lo = hr[32 * s + 2 * q], hi = hr[32 * s + 2 * q + 1];
-        float hf[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hf[i] = c16 == 0 ? lo[i] : 0.f;
-          hf[4 + i] = c16 == 0 ? hi[i] : 0.f;
-        }
-        hv[s][q] = rb_perm8(hf);
-      }
-    const RbConsts kc = rb_consts();
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const uint32_t sc = group_consts(sw, bw, s, kq >> 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hv[s][q], rb_rebuild(code[s][q], sc, kc), acc, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = hs[16 * s + q];
+      hv[s][q] = u4v{v.x, v.y, v.z, v.w};
     }
+  // B operand: tile column c16 is output column 8 cc + (c16 & 7) over the
+  // input half c16 >> 3
+  const bool use_sh = shared && live;
+  const int e = shared ? 0 : e_slot;
+  const uint32_t *wq = use_sh ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
+  const uint16_t *wsc = use_sh ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
+  const uint16_t *wbi = use_sh ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
+  const int n = 8 * cc + (c16 & 7), kh = c16 >> 3;
+  const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + (kSpan / 16) * kh + 4 * kq;
+  u4v code[kSteps / 2];
+#pragma unroll
+  for (int s = 0; s < kSteps / 2; ++s) code[s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
+  // the four groups of this half: group 2 s + (kq >> 1) of them feeds step s
+  const uint2 sw = *reinterpret_cast<const uint2 *>(wsc + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
+  const uint2 bw = *reinterpret_cast<const uint2 *>(wbi + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
+
+  const RbConsts kc = rb_consts();
+  const uint32_t sh = 16u * (uint32_t)(kq >> 1);
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kSteps / 2; ++s) {
+    const uint32_t swd = s == 0 ? sw.x : sw.y, bwd = s == 0 ? bw.x : bw.y;
+    const uint32_t sc = rb_pack_scale_bias((swd >> sh) & 0xFFFFu, (bwd >> sh) & 0xFFFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(rb_h8, hv[s][q]),
+                                                   rb_rebuild(code[s][q], sc, kc), acc, 0, 0, 0);
   }
-  // row 0, column c16 of the tile sits in lane (c16, kq = 0), element 0
-  if (kq == 0) s_part[j][c16] = acc[0];
+  // row 0 (first half) of columns 0-7 and row 1 (second half) of columns
+  // 8-15 sit in lanes 0-15 (kq = 0), elements 0 and 1
+  if (kq == 0) s_part[j][c16] = live ? (c16 < 8 ? acc[0] : acc[1]) : 0.f;
   if (lane == 0 && !shared) s_gate[j] = g_slot;
   __syncthreads();
-  if (tid < 16) {
+  if (tid < 8) {
     float y = 0.f;
-    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * s_part[jj][tid];
-    y += s_part[k][tid];
-    a.y[(int64_t)t * d + 16 * cc + tid] = y;
+    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * (s_part[jj][tid] + s_part[jj][tid + 8]);
+    y += s_part[k][tid] + s_part[k][tid + 8];
+    a.y[(int64_t)t * d + 8 * cc + tid] = y;
   }
 }
 
@@ -350,7 +354,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 g2(a.T * (a.d / 16)), b2(64 * (a.k + 1));
+  const dim3 g2(a.T * (a.d / 8)), b2(64 * (a.k + 1));
   hipExtLaunchKernelGGL(decode_dn_kernel, g2, b2, 0, s, nullptr, dn_stop, 0, a);
   return hipGetLastError();
 }

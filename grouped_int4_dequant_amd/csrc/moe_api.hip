@@ -106,7 +106,7 @@ struct Workspace {
   int32_t *units, *num_units;
   int32_t *chunk_counts;
   uint16_t *x16, *h, *h_sh, *o, *o_sh;
-  float *dec_h;  // decode-shape calls only
+  uint16_t *dec_h;  // decode-shape calls only
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
@@ -136,7 +136,7 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.o = c.take<uint16_t>((size_t)(tk + (L->f_sh > 0 ? T : 0)) * L->d);
   o.o_sh = (L->f_sh > 0 && base) ? o.o + (size_t)tk * L->d : nullptr;
   const int fmax = L->f > L->f_sh ? L->f : L->f_sh;
-  o.dec_h = T <= kDecodeMaxT ? c.take<float>((size_t)T * (L->k + 1) * fmax) : nullptr;
+  o.dec_h = T <= kDecodeMaxT ? c.take<uint16_t>((size_t)T * (L->k + 1) * fmax) : nullptr;
   if (w) *w = o;
   return (size_t)round_up((int64_t)c.off, kAlign);
 }

@@ -151,7 +151,8 @@ struct DecodeArgs {
   const uint32_t *sh_gu_q; const uint16_t *sh_gu_s, *sh_gu_b;
   const uint32_t *sh_dn_q; const uint16_t *sh_dn_s, *sh_dn_b;
   int32_t *ids; float *gates; // [T][k], written by the gate/up kernel
-  float *h;                   // fp32 [T][k+1][fmax] (slot k: shared expert)
+  uint16_t *h;                // fp16 [T][k+1][fmax] (slot k: shared expert); within each
+                              // 8 columns, the rebuild order 0,4,1,5,2,6,3,7
   float *y;                   // fp32 [T][d]
 };
 
