@@ -195,9 +195,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     s_x[tid] = x_chunk_h8(xr0);
   } else {
     // T chunks per thread, requested behind the weights: waiting for them
-    // also waits for the weights, which the MFMAs need next anyway
+    // also waits for the weights, which the MFMAs need next anyway. All
+    // requests go out before the first store (a load-store loop would wait
+    // for memory once per token); indexes past T repeat the last token.
     const uint4 *xg = reinterpret_cast<const uint4 *>(a.x);
-    for (int i = tid; i < T * nthreads; i += nthreads) s_x[i] = x_chunk_h8(xg[i]);
+    uint4 xc[kDecodeMaxT];
+#pragma unroll
+    for (int i = 0; i < kDecodeMaxT; ++i) xc[i] = xg[min(i, T - 1) * nthreads + tid];
+#pragma unroll
+    for (int i = 0; i < kDecodeMaxT; ++i)
+      if (i < T) s_x[i * nthreads + tid] = x_chunk_h8(xc[i]);
   }
   __syncthreads();
   const int tok = nth_bit(mask, c16 < nrows ? c16 : 0);
