@@ -40,6 +40,12 @@ class MoeRoutingT(ctypes.Structure):
                 ("block_map", _P), ("num_blocks", _P)]
 
 
+class MoeWorkspaceLayoutT(ctypes.Structure):
+    _fields_ = [("decode_form", _I32), ("x16", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("h_sh", ctypes.c_int64), ("o", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+                ("dec_h", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -55,6 +61,8 @@ def load() -> ctypes.CDLL:
         lib.moe_max_blocks.restype = _I32
         lib.moe_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT)]
         lib.moe_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_workspace_layout.argtypes = [_I32, ctypes.POINTER(MoeLayerT), ctypes.POINTER(MoeWorkspaceLayoutT)]
+        lib.moe_workspace_layout.restype = ctypes.c_int
         lib.moe_route_workspace_bytes.argtypes = [_I32, _I32]
         lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_route.argtypes = [_P, _I32, _I32, _I32, ctypes.POINTER(MoeRoutingT), _P,
@@ -157,6 +165,14 @@ def max_blocks(T: int, E: int, k: int) -> int:
 
 def workspace_bytes(T: int, layer: Layer) -> int:
     return int(load().moe_workspace_bytes(T, ctypes.byref(layer.c)))
+
+
+def workspace_layout(T: int, layer: Layer) -> Dict[str, int]:
+    """moe_workspace_layout: byte offsets of the fp16 intermediates a
+    moe_layer_forward call of T tokens keeps in its workspace (-1: absent)."""
+    out = MoeWorkspaceLayoutT()
+    _check(load().moe_workspace_layout(T, ctypes.byref(layer.c), ctypes.byref(out)), "moe_workspace_layout")
+    return {name: int(getattr(out, name)) for name, _ in MoeWorkspaceLayoutT._fields_}
 
 
 def route_workspace_bytes(T: int, E: int) -> int:

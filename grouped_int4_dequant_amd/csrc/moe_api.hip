@@ -37,13 +37,15 @@ constexpr int kNarrowTailDown = MOE_GEMM_NARROW_TAIL_DOWN;
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Bump allocator over the caller's workspace; with base == nullptr it only
-// measures.
+// measures. `last` is the byte offset of the most recent buffer.
 struct Carver {
   char *base;
   size_t off = 0;
+  size_t last = 0;
   template <typename T>
   T *take(size_t count) {
     off = (size_t)round_up((int64_t)off, kAlign);
+    last = off;
     T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
     off += count * sizeof(T);
     return p;
@@ -110,8 +112,13 @@ struct Workspace {
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
-size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
+// lay (nullable) receives the byte offsets of the fp16 intermediates.
+size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w,
+                   moe_workspace_layout_t *lay = nullptr) {
   Carver c{base};
+  moe_workspace_layout_t ofs{};
+  ofs.decode_form = decode_supported(T, L) ? 1 : 0;
+  ofs.x16 = ofs.h = ofs.h_sh = ofs.o = ofs.o_sh = ofs.dec_h = -1;
   const int E = L->E, k = L->k;
   const int64_t tk = (int64_t)T * k;
   Workspace o;
@@ -128,17 +135,40 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w) {
   o.num_units = c.take<int32_t>(1);
   o.chunk_counts = c.take<int32_t>((size_t)ceil_div(T, kSubChunk) * E);
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
+  ofs.x16 = (int64_t)c.last;
   // The shared expert's rows follow the routed rows in h and o when their
   // widths match, so one grouped GEMM can cover both.
   const bool joint_h = L->f_sh == L->f;
   o.h = c.take<uint16_t>((size_t)tk * L->f + (joint_h ? (size_t)T * L->f_sh : 0));
-  o.h_sh = joint_h ? (base ? o.h + (size_t)tk * L->f : nullptr) : c.take<uint16_t>((size_t)T * L->f_sh);
+  ofs.h = (int64_t)c.last;
+  if (joint_h) {
+    o.h_sh = base ? o.h + (size_t)tk * L->f : nullptr;
+    ofs.h_sh = L->f_sh > 0 ? ofs.h + 2 * tk * L->f : -1;
+  } else {
+    o.h_sh = c.take<uint16_t>((size_t)T * L->f_sh);
+    ofs.h_sh = L->f_sh > 0 ? (int64_t)c.last : -1;
+  }
   o.o = c.take<uint16_t>((size_t)(tk + (L->f_sh > 0 ? T : 0)) * L->d);
+  ofs.o = (int64_t)c.last;
   o.o_sh = (L->f_sh > 0 && base) ? o.o + (size_t)tk * L->d : nullptr;
+  ofs.o_sh = L->f_sh > 0 ? ofs.o + 2 * tk * L->d : -1;
   const int fmax = L->f > L->f_sh ? L->f : L->f_sh;
-  o.dec_h = T <= kDecodeMaxT ? c.take<uint16_t>((size_t)T * (L->k + 1) * fmax) : nullptr;
+  if (ofs.decode_form) {
+    o.dec_h = c.take<uint16_t>((size_t)T * (L->k + 1) * fmax);
+    ofs.dec_h = (int64_t)c.last;
+  } else {
+    o.dec_h = nullptr;
+  }
   if (w) *w = o;
+  if (lay) *lay = ofs;
   return (size_t)round_up((int64_t)c.off, kAlign);
+}
+
+// Workspace bytes for T tokens, made non-decreasing in T: the few-token form
+// carves a buffer the prefill form does not, so a workspace sized for T also
+// covers every smaller call (a chunked call's shorter last chunk included).
+size_t layer_ws_bytes(int T, const moe_layer_t *L) {
+  return std::max(carve_layer(T, L, nullptr, nullptr), carve_layer(std::min(T, kDecodeMaxT), L, nullptr, nullptr));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -275,7 +305,7 @@ int host_route(int T, int E, int k, int unit_rows, const moe_routing_t &rt, int3
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
                 hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true}) {
-  const size_t need = carve_layer(T, L, nullptr, nullptr);
+  const size_t need = layer_ws_bytes(T, L);
   if (ws_bytes < need + (opt.unfused ? expand_bytes(L) : 0)) return MOE_EWORKSPACE;
   Workspace w;
   carve_layer(T, L, static_cast<char *>(ws), &w);
@@ -437,7 +467,13 @@ size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {
   if (!L || T < 0 || T > kMaxRouteTokens) return 0;
   if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->k > L->E || L->f_sh < 0) return 0;
   if (L->E > MOE_MAX_EXPERTS || L->k > kMaxTopK || L->d % 64 || L->f % 64 || L->f_sh % 64) return 0;
-  return carve_layer(T, L, nullptr, nullptr);
+  return layer_ws_bytes(T, L);
+}
+
+int moe_workspace_layout(int32_t T, const moe_layer_t *L, moe_workspace_layout_t *out) {
+  if (!out || moe_workspace_bytes(T, L) == 0 || T < 1) return MOE_EINVAL;
+  carve_layer(T, L, nullptr, nullptr, out);
+  return MOE_OK;
 }
 
 size_t moe_ablation_workspace_bytes(int32_t T, const moe_layer_t *L, int32_t variant) {
@@ -556,8 +592,11 @@ int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *lo
   if (T == 0) return MOE_OK;
   if (!x || !logits || !y || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
-  const int32_t c0 = std::min(chunk, T);
-  if (ws_bytes < moe_workspace_bytes(c0, L)) return MOE_EWORKSPACE;
+  // every chunk's need is checked before the first is enqueued (the
+  // workspace size is non-decreasing in T, so the first chunk's covers the
+  // shorter last one)
+  const int32_t c0 = std::min(chunk, T), tail = T - (T - 1) / chunk * chunk;
+  if (ws_bytes < moe_workspace_bytes(c0, L) || ws_bytes < moe_workspace_bytes(tail, L)) return MOE_EWORKSPACE;
   for (int32_t t0 = 0; t0 < T; t0 += chunk) {
     const int32_t n = std::min(chunk, T - t0);
     st = forward_one(L, x + (int64_t)t0 * L->d, logits + (int64_t)t0 * L->E, n,

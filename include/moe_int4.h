@@ -42,9 +42,12 @@
  * Numerics of the GPU path: each 64-weight group is rebuilt in registers as
  * fp16 values fp16(s*(q-8) + (b+8s)), which is within one fp16 rounding of
  * s*q + b for scales of at least 2^-14; activations enter the matrix cores as
- * fp16 (bf16 inputs convert exactly while |x| < 65504) and products accumulate
- * in fp32. The expert intermediates h and the expert outputs are held as
- * fp16 (so they must stay below 65504 in magnitude); y is fp32.
+ * fp16 and products accumulate in fp32. A bf16 x converts to fp16 exactly
+ * when x == 0 or 2^-17 <= |x| <= 65280 (the largest bf16 value below fp16's
+ * overflow); smaller magnitudes round to fp16's subnormal spacing 2^-24 (below
+ * 2^-25 to zero) and |x| >= 65536 becomes infinite. The expert intermediates
+ * h and the expert outputs are held as fp16 (they must stay below 65520 in
+ * magnitude or they become infinite); y is fp32.
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H
@@ -124,11 +127,39 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
  * Bytes of device workspace moe_layer_forward needs for T tokens of layer L
  * (routing scratch, the fp16 activation copy, the fp16 expert
  * intermediates and the fp16 expert outputs; about 102 MB at T=2048,
- * d=2048, f=512, E=256, k=8).
+ * d=2048, f=512, E=256, k=8). Non-decreasing in T, so a workspace sized for
+ * T serves every call of fewer tokens.
  * moe_prefill_chunked needs moe_workspace_bytes(chunk, L). Host-only: reads
  * the scalar fields of L. Returns 0 when the arguments are invalid.
  */
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L);
+
+/*
+ * Where a moe_layer_forward call of T tokens keeps its fp16 intermediates
+ * inside the workspace, for tests and debugging (the values are those the
+ * layer's numerics rest on: activations entering the matrix cores, the SwiGLU
+ * output h and each expert's output o). Byte offsets from the workspace start;
+ * -1 where the buffer does not exist. Host-only; MOE_EINVAL for T < 1, a null
+ * out or an invalid layer. After a call on the prefill form completes on its
+ * stream:
+ *   x16   fp16 [T][d]      x rounded to fp16
+ *   h     fp16 [T*k][f]    SwiGLU output per expert-sorted row (row p is
+ *                          sorted pair p)
+ *   h_sh  fp16 [T][f_sh]   the shared expert's SwiGLU output
+ *   o     fp16 [T*k][d]    expert output per expert-sorted row
+ *   o_sh  fp16 [T][d]      the shared expert's output
+ * x16, h and h_sh store each run of 8 columns in the order 0,4,1,5,2,6,3,7;
+ * o and o_sh are in natural order. decode_form is 1 when the call takes the
+ * few-token form; then only
+ *   dec_h fp16 [T][k+1][max(f, f_sh)]  h per (token, slot), slot k the shared
+ *                          expert, 8-runs permuted as above
+ * holds data (x16, h and o are not written).
+ */
+typedef struct moe_workspace_layout {
+  int32_t decode_form;
+  int64_t x16, h, h_sh, o, o_sh, dec_h;
+} moe_workspace_layout_t;
+int moe_workspace_layout(int32_t T, const moe_layer_t *L, moe_workspace_layout_t *out);
 
 /* Bytes of device workspace moe_route needs for T tokens over E experts (the
  * per-64-token expert counts; 32 KiB at T=2048, E=256). Host-only; 0 on

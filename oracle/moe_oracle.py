@@ -36,11 +36,20 @@ the shared expert is added with weight 1; the activation is SwiGLU with gate
 rows first; the scatter is stable in ascending pair index t*k+j; the block map
 holds (expert, first row, row count) triples over unpadded offsets.
 
+Diagnostic mode (not part of the method): emulate="fp16" rounds to the
+nearest fp16 exactly the values the GPU path stores in fp16 (the rebuilt
+weights, x entering the matrix cores, h and each expert's output o) and keeps
+everything else exact, so a correct GPU result is within a few fp16 roundings
+of it element by element; tests use it to catch indexing mistakes that the
+5e-3 relative tolerance against the exact result would hide.
+
 Parity pins (tests/test_oracle_pins.py) tie every step to something other than
 this code: hand-packed words, a brute-force top-k, library-routine special
 cases, the per-group affine identity, closed-form SwiGLU layers, linearity,
-equivariance and the dense masked form of the combine. Full-size expert FFN
-values are pinned only through those identities (parity unpinned beyond them).
+equivariance, the dense masked form of the combine, hand-computed error
+metrics, IEEE binary16 rounding facts and a pure-Python brute force of the
+fp16 emulation. Full-size expert FFN values are pinned only through those
+identities (parity unpinned beyond them).
 
 Pages cited (titles as published):
   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine for
@@ -207,78 +216,122 @@ def route(logits, k: int) -> Dict[str, np.ndarray]:
 
 
 # -------------------------------------------------------------- expert FFN ---
-def _round(a: np.ndarray, fmt: Optional[str]) -> np.ndarray:
-    """Diagnostic rounding (not part of the method): emulate storing an
-    intermediate in bf16 or fp16 with round-to-nearest-even."""
-    if fmt is None:
-        return a
-    if fmt == "fp16":
-        return a.astype(np.float16).astype(np.float64)
-    if fmt == "bf16":
-        u = a.astype(np.float32).view(np.uint32)
-        u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
-        return u.view(np.float32).astype(np.float64)
-    raise ValueError(fmt)
-
-
-def swiglu_ffn(X, gu_w, dn_w, round_w: Optional[str] = None,
-               round_h: Optional[str] = None) -> np.ndarray:
-    """Step 9 for a batch of rows of one expert: a = X W_gu^T (gate columns
-    0..f-1, up columns f..2f-1), h = silu(gate) * up, o = h W_dn^T.
-    X float64 [m, d]; gu_w float64 [2f, d]; dn_w float64 [d, f]. round_w and
-    round_h are diagnostics that emulate reduced-precision storage."""
+def swiglu_h(X, gu_w) -> np.ndarray:
+    """Step 9, first half, for a batch of rows of one expert: a = X W_gu^T
+    (gate columns 0..f-1, up columns f..2f-1) and h = silu(gate) * up, with
+    silu(z) = z / (1 + exp(-z)). X float64 [m, d]; gu_w float64 [2f, d]."""
     f = gu_w.shape[0] // 2
-    a = X @ _round(gu_w, round_w).T
+    a = np.asarray(X, np.float64) @ np.asarray(gu_w, np.float64).T
     gate, up = a[:, :f], a[:, f:]
-    h = gate / (1.0 + np.exp(-gate)) * up
-    return _round(h, round_h) @ _round(dn_w, round_w).T
+    return gate / (1.0 + np.exp(-gate)) * up
 
 
-def expert_weights(layer: Dict[str, np.ndarray], e) -> Tuple[np.ndarray, np.ndarray]:
+def down_proj(h, dn_w) -> np.ndarray:
+    """Step 9, second half: o = h W_dn^T. h float64 [m, f]; dn_w float64 [d, f]."""
+    return np.asarray(h, np.float64) @ np.asarray(dn_w, np.float64).T
+
+
+def swiglu_ffn(X, gu_w, dn_w) -> np.ndarray:
+    """Step 9 for a batch of rows of one expert: o = (silu(X W_g^T) * X W_u^T) W_dn^T."""
+    return down_proj(swiglu_h(X, gu_w), dn_w)
+
+
+# ------------------------------------------------- fp16 storage emulation ---
+# A diagnostic, not part of the method. The GPU path keeps four kinds of
+# values in fp16: the rebuilt weights, the activations entering the matrix
+# cores, the SwiGLU output h and each expert's output o (y stays fp32). With
+# emulate="fp16" the oracle rounds exactly those values to the nearest fp16
+# (ties to even) and computes everything else exactly, so its result differs
+# from a correct GPU result only by the GPU's fp32 accumulation and by the
+# occasional fp16 rounding that this accumulation sends the other way.
+def round_fp16(a) -> np.ndarray:
+    """Nearest fp16 value of float64 values (ties to even), as float64.
+    Magnitudes of 65520 and above become infinite, as in IEEE binary16."""
+    with np.errstate(over="ignore"):
+        return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
+
+
+def ulp_fp16(a) -> np.ndarray:
+    """Spacing of fp16 numbers at |a|: 2^(e - 10) for 2^e <= |a| < 2^(e+1)
+    with e >= -14, and 2^-24 (the subnormal spacing) below 2^-14."""
+    av = np.abs(np.asarray(a, np.float64))
+    m, e = np.frexp(av)  # |a| = m 2^e with 0.5 <= m < 1 (frexp gives e = 0 for 0)
+    e = np.where(av == 0.0, -24 + 11, e)
+    return np.ldexp(1.0, np.maximum(e - 11, -24))
+
+
+def expert_weights(layer: Dict[str, np.ndarray], e, emulate: Optional[str] = None
+                   ) -> Tuple[np.ndarray, np.ndarray]:
     """Dequantised (gate/up, down) weights of routed expert e, or of the shared
-    expert when e == "sh"."""
+    expert when e == "sh"; rounded to fp16 when emulate == "fp16"."""
     if e == "sh":
-        return (dequant(layer["sh_gu_q"], layer["sh_gu_s"], layer["sh_gu_b"]),
-                dequant(layer["sh_dn_q"], layer["sh_dn_s"], layer["sh_dn_b"]))
-    return (dequant(layer["gu_q"][e], layer["gu_s"][e], layer["gu_b"][e]),
-            dequant(layer["dn_q"][e], layer["dn_s"][e], layer["dn_b"][e]))
+        ws = (dequant(layer["sh_gu_q"], layer["sh_gu_s"], layer["sh_gu_b"]),
+              dequant(layer["sh_dn_q"], layer["sh_dn_s"], layer["sh_dn_b"]))
+    else:
+        ws = (dequant(layer["gu_q"][e], layer["gu_s"][e], layer["gu_b"][e]),
+              dequant(layer["dn_q"][e], layer["dn_s"][e], layer["dn_b"][e]))
+    if emulate == "fp16":
+        return round_fp16(ws[0]), round_fp16(ws[1])
+    if emulate is not None:
+        raise ValueError(emulate)
+    return ws
 
 
-def moe_forward(layer: Dict[str, np.ndarray], x_bits, logits, k: int,
-                tokens: Optional[Sequence[int]] = None,
-                round_w: Optional[str] = None, round_h: Optional[str] = None,
-                weight_cache: Optional[dict] = None) -> np.ndarray:
-    """Steps 3, 4 and 9-11: y_t = sum_j g_tj * FFN_(e_tj)(x_t) + FFN_sh(x_t)
-    for the listed tokens (all by default). Returns float64 [len(tokens), d].
+def moe_forward_terms(layer: Dict[str, np.ndarray], x_bits, logits, k: int,
+                      tokens: Optional[Sequence[int]] = None,
+                      emulate: Optional[str] = None,
+                      weight_cache: Optional[dict] = None) -> Dict[str, np.ndarray]:
+    """Steps 3, 4 and 9-11 for the listed tokens (all by default), with the
+    terms of the combine kept: g [n][k] (gates), o [n][k][d] (routed expert
+    outputs by slot), o_sh [n][d] (shared expert output, None without one) and
+    y [n][d] = sum_j g_j o_j + o_sh, the slots added in order j = 0..k-1.
 
     Tokens are independent, so any subset gives exactly the rows the full call
-    would. Work is grouped by expert only to dequantise each expert once."""
+    would. Work is grouped by expert only to dequantise each expert once.
+    emulate="fp16" rounds the weights, x, h and o to fp16 (diagnostic)."""
     L = np.asarray(logits, dtype=np.float32)
     T = L.shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     X = bf16_value(np.asarray(x_bits)[tok])
+    rnd = round_fp16 if emulate == "fp16" else (lambda v: v)
+    X = rnd(X)
     ids = topk(L[tok], k)
     g = gates(L[tok], ids)
     n, d = X.shape
-    Y = np.zeros((n, d), np.float64)
     cache = {} if weight_cache is None else weight_cache
 
     def weights(e):
-        if e not in cache:
-            cache[e] = expert_weights(layer, e)
-        return cache[e]
+        key = (e, emulate)
+        if key not in cache:
+            cache[key] = expert_weights(layer, e, emulate)
+        return cache[key]
 
-    # routed experts: per token, terms are added in slot order j = 0..k-1
+    def ffn(rows, e):
+        gu, dn = weights(e)
+        return rnd(down_proj(rnd(swiglu_h(X[rows], gu)), dn))
+
+    o = np.zeros((n, k, d), np.float64)
     for j in range(k):
         for e in np.unique(ids[:, j]):
             rows = np.nonzero(ids[:, j] == e)[0]
-            gu, dn = weights(int(e))
-            o = swiglu_ffn(X[rows], gu, dn, round_w, round_h)
-            Y[rows] += g[rows, j][:, None] * o
+            o[rows, j] = ffn(rows, int(e))
+    Y = np.zeros((n, d), np.float64)
+    for j in range(k):  # slot order
+        Y += g[:, j][:, None] * o[:, j]
+    o_sh = None
     if "sh_gu_q" in layer:  # step 10: shared expert, weight 1
-        gu, dn = weights("sh")
-        Y += swiglu_ffn(X, gu, dn, round_w, round_h)
-    return Y
+        o_sh = ffn(np.arange(n), "sh")
+        Y += o_sh
+    return dict(y=Y, g=g, o=o, o_sh=o_sh)
+
+
+def moe_forward(layer: Dict[str, np.ndarray], x_bits, logits, k: int,
+                tokens: Optional[Sequence[int]] = None,
+                emulate: Optional[str] = None,
+                weight_cache: Optional[dict] = None) -> np.ndarray:
+    """Steps 3, 4 and 9-11: y_t = sum_j g_tj * FFN_(e_tj)(x_t) + FFN_sh(x_t)
+    for the listed tokens (all by default). Returns float64 [len(tokens), d]."""
+    return moe_forward_terms(layer, x_bits, logits, k, tokens, emulate, weight_cache)["y"]
 
 
 def moe_forward_sorted(layer: Dict[str, np.ndarray], x_bits, logits, k: int) -> np.ndarray:
@@ -316,7 +369,10 @@ def route_chunks(logits, k: int, chunk: int) -> List[Dict[str, np.ndarray]]:
 
 
 def error_metrics(y_test, y_ref) -> Dict[str, float]:
-    """Relative Frobenius error and max abs error over rms(reference)."""
+    """Acceptance metrics of a result against the reference:
+    rel_fro = ||y_test - y_ref||_F / ||y_ref||_F and
+    max_over_rms = max |y_test - y_ref| / rms(y_ref), where
+    rms(y_ref) = ||y_ref||_F / sqrt(number of elements)."""
     yt = np.asarray(y_test, np.float64)
     yr = np.asarray(y_ref, np.float64)
     fro = float(np.linalg.norm(yr))

@@ -145,3 +145,52 @@ def test_route_and_gemm_reject_bad_arguments():
     assert g(*bad) == B.MOE_EINVAL
     bad = list(args); bad[10] = 0
     assert g(*bad) == B.MOE_OK  # no blocks: nothing to do
+
+
+def test_workspace_size_is_non_decreasing_in_tokens():
+    """A workspace sized for T serves every smaller call: the few-token form's
+    extra buffer must not make T = 8 need more than T = 9."""
+    lib = moe.load()
+    for shape in (dict(), dict(E=16, k=2), dict(f_sh=0)):
+        L = qwen_layer_struct(**shape)
+        sizes = [lib.moe_workspace_bytes(t, ctypes.byref(L)) for t in range(0, 40)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), (shape, sizes)
+
+
+def test_chunked_driver_checks_every_chunk_before_enqueueing():
+    """17 tokens in chunks of 9: the 8-token tail takes the few-token form;
+    a workspace one byte short of the larger need is rejected up front."""
+    L = qwen_layer_struct()
+    lib = moe.load()
+    need = max(lib.moe_workspace_bytes(9, ctypes.byref(L)), lib.moe_workspace_bytes(8, ctypes.byref(L)))
+    assert lib.moe_workspace_bytes(9, ctypes.byref(L)) == need
+    st = lib.moe_prefill_chunked(ctypes.byref(L), 0x1000, 0x1000, 17, 9, 0x1000, 0x1000, need - 1, None)
+    assert st == B.MOE_EWORKSPACE
+
+
+def test_workspace_layout_offsets():
+    lib = moe.load()
+    T, d, f, k, f_sh = 2048, 2048, 512, 8, 512
+    L = qwen_layer_struct()
+    out = B.MoeWorkspaceLayoutT()
+    assert lib.moe_workspace_layout(T, ctypes.byref(L), ctypes.byref(out)) == B.MOE_OK
+    ws = lib.moe_workspace_bytes(T, ctypes.byref(L))
+    assert out.decode_form == 0 and out.dec_h == -1
+    for off in (out.x16, out.h, out.o):
+        assert off >= 0 and off % 256 == 0
+    assert out.x16 + 2 * T * d <= out.h
+    assert out.h_sh == out.h + 2 * T * k * f          # shared rows follow the routed rows
+    assert out.o_sh == out.o + 2 * T * k * d
+    assert out.o_sh + 2 * T * d <= ws
+    assert lib.moe_workspace_layout(1, ctypes.byref(L), ctypes.byref(out)) == B.MOE_OK
+    assert out.decode_form == 1 and 0 <= out.dec_h and out.dec_h + 2 * (k + 1) * f <= lib.moe_workspace_bytes(1, ctypes.byref(L))
+    assert lib.moe_workspace_layout(0, ctypes.byref(L), ctypes.byref(out)) == B.MOE_EINVAL
+    assert lib.moe_workspace_layout(4, ctypes.byref(L), None) == B.MOE_EINVAL
+    bad = qwen_layer_struct(d=2000)
+    assert lib.moe_workspace_layout(4, ctypes.byref(bad), ctypes.byref(out)) == B.MOE_EINVAL
+    L2 = qwen_layer_struct(f_sh=1024)                 # shared width differs: separate buffer
+    assert lib.moe_workspace_layout(100, ctypes.byref(L2), ctypes.byref(out)) == B.MOE_OK
+    assert out.h_sh >= out.h + 2 * 100 * k * f
+    L3 = qwen_layer_struct(f_sh=0)
+    assert lib.moe_workspace_layout(100, ctypes.byref(L3), ctypes.byref(out)) == B.MOE_OK
+    assert out.h_sh == -1 and out.o_sh == -1

@@ -2,9 +2,8 @@
 
 Routing tensors must match bit for bit; router weights within 1e-6; layer
 outputs within relative Frobenius error 5e-3 and max abs error 2e-2 * rms of
-the oracle output. Large configurations compare every routing tensor and a
-sample of output rows (tokens are independent, so sampled rows are exact
-oracle rows)."""
+the oracle output, every row (the full-size configurations and the
+fp16-emulation and stage checks are in test_gpu_emulation.py)."""
 import sys
 
 import numpy as np
@@ -215,22 +214,6 @@ def test_layer_all_tokens_one_expert_set(moe):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, 2), "dense special case")
 
 
-def _sample(T, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n, replace=False)]))
-
-
-@pytest.mark.parametrize("index", [1, 2])
-def test_layer_full_config(moe, index):
-    p = S.make_problem(index)
-    say(f"layer config {index} T={p.T} (routing full, outputs sampled)")
-    y, routing = run_layer(moe, p)
-    check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
-    tok = _sample(p.T, seed=index)
-    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
-    check_output(y[tok], y_ref, f"config {index} sampled")
-
-
 @pytest.mark.parametrize("index", [1, 2])
 def test_layer_bit_reproducible(moe, index):
     """Repeated calls on the same inputs give the same y bit for bit (every
@@ -247,24 +230,6 @@ def test_layer_bit_reproducible(moe, index):
         torch.cuda.synchronize()
         diff = (y != first).sum().item()
         assert diff == 0, f"repeat {r}: {diff} output elements differ"
-
-
-def test_chunked_config3(moe):
-    p = S.make_problem(3)
-    say("config 3: T=8192 in 2048-token chunks (skewed)")
-    layer, x, lg = upload(p, moe)
-    y = moe.prefill_chunked(layer, x, lg, chunk=2048)
-    torch.cuda.synchronize()
-    y = y.cpu().numpy()
-    ref_chunks = O.route_chunks(p.logits, p.shape.k, 2048)
-    for c, ref in enumerate(ref_chunks):
-        got = moe.route(lg[c * 2048:(c + 1) * 2048].contiguous(), p.shape.k)
-        torch.cuda.synchronize()
-        check_routing(got, ref, 2048, p.shape.k)
-        say(f"  chunk {c}: touched experts {int((ref['counts'] > 0).sum())}, max rows {int(ref['counts'].max())}")
-    tok = _sample(p.T, n=64, seed=3)
-    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
-    check_output(y[tok], y_ref, "config 3 sampled")
 
 
 @pytest.mark.parametrize("T", [1, 4])
@@ -414,15 +379,13 @@ def test_ablation_matches_oracle(moe, variant, T, d, f, E, k, f_sh):
 @pytest.mark.parametrize("variant", ["tile16", "host_routing", "unfused"])
 def test_ablation_full_config(moe, variant):
     p = S.make_problem(1)
-    say(f"ablation {variant} config 1 T={p.T} (routing full, outputs sampled)")
+    say(f"ablation {variant} config 1 T={p.T} (every row)")
     layer, x, lg = upload(p, moe)
     routing = moe.alloc_routing(p.T, p.shape.E, p.shape.k)
     y = moe.layer_forward_ablation(layer, x, lg, variant, routing=routing)
     torch.cuda.synchronize()
     check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
-    tok = _sample(p.T, seed=11)
-    y_ref = O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
-    check_output(y.cpu().numpy()[tok], y_ref, f"{variant} config 1 sampled")
+    check_output(y.cpu().numpy(), O.moe_forward(p.layer, p.x, p.logits, p.shape.k), f"{variant} config 1")
 
 
 def test_zero_tokens_is_a_noop(moe):

@@ -458,11 +458,11 @@ def _mut_tie_high_index(L, k):
                      for t in range(L.shape[0])], np.int32)
 
 
-def _mut_gate_up_swapped(X, gu_w, dn_w, round_w=None, round_h=None):
+def _mut_gate_up_swapped(X, gu_w):
     f = gu_w.shape[0] // 2
     a = X @ gu_w.T
     up, gate = a[:, :f], a[:, f:]
-    return (gate / (1 + np.exp(-gate)) * up) @ dn_w.T
+    return gate / (1 + np.exp(-gate)) * up
 
 
 def _mut_unstable_scatter(ids, offs):
@@ -495,7 +495,7 @@ def _mut_router_expert_shift(x_bits, w_bits):
     ("dequant", _mut_no_bias),
     ("dequant", _mut_group_mod),
     ("topk", _mut_tie_high_index),
-    ("swiglu_ffn", _mut_gate_up_swapped),
+    ("swiglu_h", _mut_gate_up_swapped),
     ("scatter", _mut_unstable_scatter),
     ("block_map", _mut_block_16),
 ])
