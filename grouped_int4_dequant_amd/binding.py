@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
                                                    ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P,
                                                    _I32]
         lib.moe_layer_forward_ablation.restype = ctypes.c_int
+        lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
+                                                  ctypes.POINTER(MoeRoutingT), _P]
+        lib.moe_layer_forward_noalloc.restype = ctypes.c_int
         lib.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         lib.moe_router_logits.restype = ctypes.c_int
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
@@ -255,6 +258,23 @@ def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
                                     y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
                                     ws.data_ptr(), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+def layer_forward_noalloc(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
+                          y: Optional[torch.Tensor] = None,
+                          routing: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> torch.Tensor:
+    """moe_layer_forward_noalloc: the layer with the library's static per-GPU
+    scratch array as its workspace (no device allocation in the call)."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(logits, "logits", torch.float32, (T, layer.E))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                            y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
+                                            _stream(stream)), "moe_layer_forward_noalloc")
     return y
 
 

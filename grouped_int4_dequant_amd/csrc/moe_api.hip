@@ -11,6 +11,7 @@
 #include "moe_internal.h"
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 using namespace moe;
@@ -604,6 +605,62 @@ int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *lo
     if (st != MOE_OK) return st;
   }
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Workspace for callers that cannot allocate: one static device array per GPU
+// the library runs on, held until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory; its device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is handed to kernels.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (nullptr on failure).
+void *device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_noalloc(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                              float *y, const moe_routing_t *routing, hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y)) return MOE_EINVAL;
+  if (layer_ws_bytes(T, L) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  // the stream must belong to the current device, whose scratch array is used
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_EHIP;
+    if ((int)sdev != dev) return MOE_EINVAL;
+  }
+  void *ws = device_scratch(dev);
+  if (!ws) return MOE_EHIP;
+  return forward_one(L, x, logits, T, y, routing, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 const char *moe_status_string(int status) {

@@ -244,6 +244,32 @@ int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logi
                       void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same kernels and results as moe_layer_forward (bit for bit),
+ * with the workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends. The call allocates nothing (no hipMalloc, no hipFree);
+ * its first call on a device looks up that device's array once.
+ *   - stream must belong to the current device (else MOE_EINVAL); the
+ *     current device's array is used.
+ *   - T is limited by moe_workspace_bytes(T, L) <= MOE_NOALLOC_SCRATCH_BYTES
+ *     (about 1300 tokens at d=2048, f=512, E=256, k=8); a larger call returns
+ *     MOE_EWORKSPACE before anything is enqueued. Longer prompts go through
+ *     moe_prefill_chunked with a caller workspace.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; nothing in it needs to start at zero (each kernel
+ *     writes what it reads before reading it). Calls that overlap on one GPU
+ *     (streams not ordered against each other) race on the array: the caller
+ *     must order them.
+ * Other arguments and errors as moe_layer_forward (MOE_EHIP also when the
+ * array's address cannot be obtained).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                              float *y, const moe_routing_t *routing, hipStream_t stream);
+
+/*
  * moe_layer_forward with stage timing, for measurement. The events are
  * attached to the kernel dispatches themselves (no marker packets between
  * kernels, so timing adds no idle time): events[0] at the start of the top-k
