@@ -433,29 +433,77 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events, T=1):
             "frac_hbm_gpu": b / gpu / 1e9 / HBM_PEAK_GBPS, "peak_gbps": HBM_PEAK_GBPS}
 
 
-def cpu_baseline(p, ntok):
-    """The fp64 oracle as it stands, on the first ntok tokens of the same
-    workload (their routed experts and the shared expert, dequantisation
-    included), scaled to tokens/s."""
-    from oracle import moe_oracle as O
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return "unknown"
+
+
+def _oracle_seconds(O, p, tokens, k, passes=1):
+    """Wall seconds per pass of the oracle's layer computation (input
+    generation excluded) on the listed tokens."""
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        O.moe_forward(p.layer, p.x, p.logits, k, tokens=tokens)
+    return (time.perf_counter() - t0) / passes
+
+
+def cpu_baseline(p, ntok):
+    """The fp64 oracle as it stands, timed on this host: the headline value is
+    the T=2048 workload (the first ntok tokens, whole passes until at least
+    10 s), scaled to tokens/s, with BLAS on every core this process may run
+    on. `configs` adds each workload on all cores and, for the 64- and
+    512-token layers, the 2048-token chunk 1 of the skewed prompt and the
+    decode step, on one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import moe_oracle as O
+    from synth import moe_inputs as S
+    cores = len(os.sched_getaffinity(0))
     ntok = min(ntok, p.T)
     tok = np.arange(ntok)
-    passes, t0 = 0, time.perf_counter()
-    while True:  # whole passes until at least 10 s of CPU work
-        O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0:
-            break
+    with threadpool_limits(limits=cores):
+        passes, t0 = 0, time.perf_counter()
+        while True:  # whole passes until at least 10 s of CPU work
+            O.moe_forward(p.layer, p.x, p.logits, p.shape.k, tokens=tok)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0:
+                break
+        rows = {}
+        for ci in (0, 1, 3):
+            q = S.make_problem(ci)
+            sec = _oracle_seconds(O, q, None, q.shape.k)
+            rows[q.config.name] = {"T": q.T, "threads": cores, "seconds": sec, "tokens_per_s": q.T / sec}
+        rows["prefill2048"] = {"T": p.T, "threads": cores, "seconds": dt / passes * p.T / ntok,
+                               "tokens_per_s": ntok * passes / dt}
+        dec = list(S.decode_steps(1, steps=41))
+        checked = [dec[i] for i in (0, 20, 40)]
+        sec = sum(_oracle_seconds(O, q, None, q.shape.k) for q in checked) / len(checked)
+        rows["decode_t1"] = {"T": 1, "threads": cores, "seconds_per_step": sec, "steps_timed": 3}
+    one = {}
+    with threadpool_limits(limits=1):
+        for ci in (0, 1):
+            q = S.make_problem(ci)
+            sec = _oracle_seconds(O, q, None, q.shape.k)
+            one[q.config.name] = {"T": q.T, "threads": 1, "seconds": sec, "tokens_per_s": q.T / sec}
+        q = S.make_problem(3)
+        sec = _oracle_seconds(O, q, np.arange(2048, 4096), q.shape.k)
+        one["skew8192_chunk1"] = {"T": 2048, "threads": 1, "seconds": sec, "tokens_per_s": 2048 / sec}
+        sec = sum(_oracle_seconds(O, c, None, c.shape.k) for c in checked) / len(checked)
+        one["decode_t1"] = {"T": 1, "threads": 1, "seconds_per_step": sec, "steps_timed": 3}
     what = f"all {p.T} tokens" if ntok == p.T else f"first {ntok} of {p.T} tokens"
-    return {"value": ntok * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} of the T={p.T} workload, {passes} pass(es) of the fp64 numpy oracle, "
-                      f"each dequantising every expert the tokens touch ({dt:.1f} s in total)"}
+    return {"value": ntok * passes / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "affinity_cpus": cores,
+            "sample": f"{what} of the T={p.T} workload, {passes} pass(es) of the fp64 numpy oracle on "
+                      f"{cores} BLAS threads, each dequantising every expert the tokens touch "
+                      f"({dt:.1f} s in total)",
+            "configs_all_cores": rows, "configs_one_thread": one}
 
 
 if __name__ == "__main__":

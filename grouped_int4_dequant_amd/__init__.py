@@ -4,11 +4,13 @@ The layer runs in hand-written HIP kernels for gfx950 behind the C ABI of
 include/moe_int4.h (libmoe_int4.so); this package is the thin ctypes binding.
 """
 from .binding import (ABLATIONS, Layer, ablation_workspace_bytes, alloc_routing, alloc_workspace,
-                      grouped_gemm_int4, layer_forward, layer_forward_ablation, layer_forward_noalloc, load, max_blocks,
+                      OVERFLOW_H, OVERFLOW_O, OVERFLOW_X, grouped_gemm_int4, layer_forward, layer_forward_ablation,
+                      layer_forward_checked, layer_forward_noalloc, load, max_blocks,
                       prefill_chunked, route, route_workspace_bytes, router_logits, status_string,
                       workspace_bytes, workspace_layout)
 
 __all__ = ["ABLATIONS", "Layer", "ablation_workspace_bytes", "alloc_routing", "alloc_workspace",
-           "grouped_gemm_int4", "layer_forward", "layer_forward_ablation", "layer_forward_noalloc", "load", "max_blocks",
+           "OVERFLOW_H", "OVERFLOW_O", "OVERFLOW_X", "grouped_gemm_int4", "layer_forward", "layer_forward_ablation",
+           "layer_forward_checked", "layer_forward_noalloc", "load", "max_blocks",
            "prefill_chunked", "route", "route_workspace_bytes", "router_logits", "status_string",
            "workspace_bytes", "workspace_layout"]

@@ -83,6 +83,9 @@ def load() -> ctypes.CDLL:
         lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
                                                   ctypes.POINTER(MoeRoutingT), _P]
         lib.moe_layer_forward_noalloc.restype = ctypes.c_int
+        lib.moe_layer_forward_checked.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
+                                                  ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P, _P]
+        lib.moe_layer_forward_checked.restype = ctypes.c_int
         lib.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         lib.moe_router_logits.restype = ctypes.c_int
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
@@ -258,6 +261,31 @@ def layer_forward(layer: Layer, x: torch.Tensor, logits: torch.Tensor,
                                     y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
                                     ws.data_ptr(), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+OVERFLOW_X, OVERFLOW_H, OVERFLOW_O = 1, 2, 4
+
+
+def layer_forward_checked(layer: Layer, x: torch.Tensor, logits: torch.Tensor, overflow: torch.Tensor,
+                          y: Optional[torch.Tensor] = None,
+                          routing: Optional[Dict[str, torch.Tensor]] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_layer_forward_checked: the layer, ORing OVERFLOW_* bits into the
+    int32 device tensor `overflow` (one element, set by the caller) when a
+    value kept in fp16 leaves fp16's finite range."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(logits, "logits", torch.float32, (T, layer.E))
+    _need(overflow, "overflow", torch.int32, (1,))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load().moe_layer_forward_checked(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                            y.data_ptr(), ctypes.byref(rs) if rs is not None else None,
+                                            ws.data_ptr(), ws.numel(), _stream(stream), overflow.data_ptr()),
+           "moe_layer_forward_checked")
     return y
 
 

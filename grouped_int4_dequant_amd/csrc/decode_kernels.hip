@@ -192,7 +192,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   // issued first), converted once per workgroup; then row c16's fragments:
   // a token of the mask, else the first one again (a row never read)
   if (ONE) {
-    s_x[tid] = x_chunk_h8(xr0);
+    const uint4 xc = x_chunk_h8(xr0);
+    s_x[tid] = xc;
+    if (blockIdx.x == 0)
+      note_overflow(a.overflow, f16x2_nonfinite(xc.x) || f16x2_nonfinite(xc.y) || f16x2_nonfinite(xc.z) ||
+                                    f16x2_nonfinite(xc.w), MOE_OVERFLOW_X);
   } else {
     // T chunks per thread, requested behind the weights: waiting for them
     // also waits for the weights, which the MFMAs need next anyway. All
@@ -204,7 +208,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
     for (int i = 0; i < kDecodeMaxT; ++i) xc[i] = xg[min(i, T - 1) * nthreads + tid];
 #pragma unroll
     for (int i = 0; i < kDecodeMaxT; ++i)
-      if (i < T) s_x[i * nthreads + tid] = x_chunk_h8(xc[i]);
+      if (i < T) {
+        const uint4 h8 = x_chunk_h8(xc[i]);
+        s_x[i * nthreads + tid] = h8;
+        if (blockIdx.x == 0)
+          note_overflow(a.overflow, f16x2_nonfinite(h8.x) || f16x2_nonfinite(h8.y) || f16x2_nonfinite(h8.z) ||
+                                        f16x2_nonfinite(h8.w), MOE_OVERFLOW_X);
+      }
   }
   __syncthreads();
   const int tok = nth_bit(mask, c16 < nrows ? c16 : 0);
@@ -257,8 +267,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
         const int slot = shared ? k : ONE ? u : s_uslot[u][t];
         // fp16, each 8 columns in the rebuild order, as the down MFMAs take it
         const int n = 16 * hc + c16;
+        const float hv = g / (1.f + __expf(-g)) * up;
+        note_overflow(a.overflow, f16_out_of_range(hv), MOE_OVERFLOW_H);
         a.h[((int64_t)t * (k + 1) + slot) * a.fmax + (n & ~7) + 2 * (n & 3) + ((n >> 2) & 1)] =
-            __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + __expf(-g)) * up));
+            __builtin_bit_cast(uint16_t, (_Float16)hv);
       }
     }
   }

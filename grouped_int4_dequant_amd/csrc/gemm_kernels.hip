@@ -131,7 +131,8 @@ struct Unit {
 
 // NRB = 16-row MFMA blocks of the unit (1..6), fixed at compile time so a K
 // step is one branch-free block the compiler can schedule as a whole.
-template <int MODE, bool AF16, bool WX, int NRB, int CB>
+// CHECK: report fp16 values out of range through P.overflow (epilogues).
+template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
   constexpr int kMaxRB = NRB;
@@ -442,6 +443,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     // part in the barriers.
     constexpr int kHCols = kCols / 2;
     lds_barrier();
+    bool bad = false;
     if (active) {
 #pragma unroll
       for (int rb = 0; rb < kMaxRB; ++rb) {
@@ -453,12 +455,14 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
             const int r = 16 * rb + 4 * kq + i;
             const float g = acc[rb][cb][i], u = acc[rb][cb + kHalf][i];
             const float h = g / (1.f + __expf(-g)) * u;
+            if (CHECK) bad |= r < nr && f16_out_of_range(h);
             *reinterpret_cast<uint16_t *>(lds + r * 256 + 16 * ((lc >> 3) ^ (r & 15)) + 2 * (lc & 7)) =
                 f32_to_f16_bits(h);
           }
         }
       }
     }
+    if (CHECK) note_overflow(P.overflow, bad, MOE_OVERFLOW_H);
     lds_barrier();
     constexpr int kRowLanes = kHCols / 8;
     constexpr int kRowsPerPass = kGemmThreads / kRowLanes;
@@ -485,6 +489,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     constexpr int kUnits = kCols / 4;  // 8-byte units of one tile row
     static_assert(kUnitRows * 512 <= 2 * kBufBytes, "output tile fits the activation buffers");
     lds_barrier();
+    bool bad = false;
     if (active) {
 #pragma unroll
       for (int rb = 0; rb < kMaxRB; ++rb) {
@@ -492,12 +497,16 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
           const int u = wave * 4 * kCB + 4 * cb + kq;
+          if (CHECK && r < nr)
+            bad |= f16_out_of_range(acc[rb][cb][0]) || f16_out_of_range(acc[rb][cb][1]) ||
+                   f16_out_of_range(acc[rb][cb][2]) || f16_out_of_range(acc[rb][cb][3]);
           const uint32_t lo = f32_to_f16_bits(acc[rb][cb][0]) | ((uint32_t)f32_to_f16_bits(acc[rb][cb][1]) << 16);
           const uint32_t hi = f32_to_f16_bits(acc[rb][cb][2]) | ((uint32_t)f32_to_f16_bits(acc[rb][cb][3]) << 16);
           *reinterpret_cast<uint2 *>(lds + r * 512 + 8 * (u ^ (r & 15))) = make_uint2(lo, hi);
         }
       }
     }
+    if (CHECK) note_overflow(P.overflow, bad, MOE_OVERFLOW_O);
     lds_barrier();
     // 16-byte chunk j (units 2j, 2j+1) of row r; kUnits / 2 lanes per row
     constexpr int kRowLanes = kUnits / 2;
@@ -535,7 +544,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   }
 }
 
-template <int MODE, bool AF16, bool WX>
+template <int MODE, bool AF16, bool WX, bool CHECK = false>
 __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
   __shared__ uint32_t tab[kTabGroups * kTabStride];
@@ -594,21 +603,21 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
   // (always, for expanded weights: their stages take four times the registers)
   if (WX || narrow) {
     switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, WX, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, WX, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, WX, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, WX, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, WX, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, WX, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 1: run_unit<MODE, AF16, WX, CHECK, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, WX, CHECK, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, WX, CHECK, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, WX, CHECK, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, WX, CHECK, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, WX, CHECK, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
     }
   } else {
     switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, WX, 1, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, WX, 2, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, WX, 3, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, WX, 4, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, WX, 5, kCBFull>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, WX, 6, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 1: run_unit<MODE, AF16, WX, CHECK, 1, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, WX, CHECK, 2, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, WX, CHECK, 3, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, WX, CHECK, 4, kCBFull>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, WX, CHECK, 5, kCBFull>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, WX, CHECK, 6, kCBFull>(P, U, lds, s_arow, tab); break;
     }
   }
 }
@@ -627,8 +636,18 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, h
     }
   } else if (a_f16) {
     switch (mode) {
-      case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, start, stop, 0, a); break;
-      case kStoreH: hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false>), grid, block, 0, s, start, stop, 0, a); break;
+      case kSwiGLU:
+        if (a.prob[0].overflow)
+          hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false, true>), grid, block, 0, s, start, stop, 0, a);
+        else
+          hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, start, stop, 0, a);
+        break;
+      case kStoreH:
+        if (a.prob[0].overflow)
+          hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false, true>), grid, block, 0, s, start, stop, 0, a);
+        else
+          hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false>), grid, block, 0, s, start, stop, 0, a);
+        break;
       default: hipExtLaunchKernelGGL((gemm_kernel<kStoreC, true, false>), grid, block, 0, s, start, stop, 0, a); break;
     }
   } else {

@@ -178,8 +178,10 @@ int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
                   int32_t *chunk_counts, int32_t *units, int32_t *num_units, const uint16_t *x,
-                  uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr, int unit_rows = kUnitRows) {
+                  uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr, int unit_rows = kUnitRows,
+                  uint32_t *overflow = nullptr) {
   TopkArgs ta{};
+  ta.overflow = overflow;
   ta.logits = logits;
   ta.T = T;
   ta.E = E;
@@ -305,7 +307,8 @@ int host_route(int T, int E, int k, int unit_rows, const moe_routing_t &rt, int3
 
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
-                hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true}) {
+                hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true},
+                uint32_t *overflow = nullptr) {
   const size_t need = layer_ws_bytes(T, L);
   if (ws_bytes < need + (opt.unfused ? expand_bytes(L) : 0)) return MOE_EWORKSPACE;
   Workspace w;
@@ -341,6 +344,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     a.sh_dn_q = L->sh_dn_q; a.sh_dn_s = L->sh_dn_s; a.sh_dn_b = L->sh_dn_b;
     a.ids = w.rt.topk_ids; a.gates = w.rt.topk_w;  // the workspace's own routing buffers
     a.h = w.dec_h; a.y = y;
+    a.overflow = overflow;
     hipEvent_t gu_start = (ev && !routing) ? ev[2] : nullptr;
     return hip_status(launch_decode(a, s, gu_start, ev ? ev[3] : nullptr, ev ? ev[4] : nullptr));
   }
@@ -350,10 +354,12 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     ta.logits = logits; ta.T = T; ta.E = E; ta.k = k;
     ta.topk_ids = rt.topk_ids; ta.topk_w = rt.topk_w;
     ta.x = x; ta.x16 = w.x16; ta.d = d;
+    ta.overflow = overflow;
     st = hip_status(launch_topk(ta, s));
     if (st == MOE_OK) st = host_route(T, E, k, opt.unit_rows, rt, w.units, w.num_units, s);
   } else {
-    st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev, opt.unit_rows);
+    st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev, opt.unit_rows,
+                       overflow);
   }
   if (st != MOE_OK) return st;
 
@@ -380,6 +386,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.nslices = (int)ceil_div(fs, hcols);
     p.wg_begin = nwg;
     p.H = w.h_sh; p.ldh = fs;
+    p.overflow = overflow;
     nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
   }
   {
@@ -394,6 +401,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.ntail = opt.ntail;
     p.wg_begin = nwg;
     p.H = w.h; p.ldh = f;
+    p.overflow = overflow;
     // full-width items, plus up to ntail + 14 units' extra half-width items
     nwg += problem_wgs(max_units_routed(T, k, E, opt.unit_rows) + 2 * (opt.ntail + 16), p.nslices);
   }
@@ -424,6 +432,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.nslices = (int)ceil_div(d, ocols);
     p.wg_begin = nwg;
     p.H = w.o_sh; p.ldh = d;
+    p.overflow = overflow;
     nwg += problem_wgs(ceil_div(T, opt.unit_rows), p.nslices);
   }
   {
@@ -438,6 +447,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.ntail = opt.ntail > 0 ? kNarrowTailDown : 0;  // ablation forms: no tail
     p.wg_begin = nwg;
     p.H = w.o; p.ldh = d;
+    p.overflow = overflow;
     // full-width items, plus (with a tail) up to ntail + 14 units' extra half-width items
     nwg += problem_wgs(max_units_routed(T, k, E, opt.unit_rows) + (p.ntail > 0 ? 2 * (p.ntail + 16) : 0), p.nslices);
   }
@@ -544,6 +554,21 @@ int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logi
   if (!x || !logits || !y || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
   return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_checked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                              float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                              hipStream_t stream, uint32_t *overflow) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign) || ((uintptr_t)overflow % 4)) return MOE_EINVAL;
+  return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream, nullptr,
+                     FwdOptions{kUnitRows, kNarrowTail, false, true}, overflow);
 }
 
 int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float *logits,

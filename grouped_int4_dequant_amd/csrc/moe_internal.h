@@ -34,6 +34,17 @@ constexpr int kGemmThreads = 64 * MOE_GEMM_WAVES;  // threads per workgroup of t
 constexpr int kGemmCols = 64 * MOE_GEMM_WAVES;     // weight rows of a full-width GEMM item (64 per wave)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A value the path stores in fp16 fell outside fp16's finite range (or was
+// NaN): OR `bit` into the caller's overflow word, when one was given.
+__device__ __forceinline__ bool f16_out_of_range(float v) { return !(fabsf(v) < 65520.f); }
+// Either fp16 half of a packed pair is infinite or NaN.
+__device__ __forceinline__ bool f16x2_nonfinite(uint32_t p) {
+  return (p & 0x7C00u) == 0x7C00u || (p & 0x7C000000u) == 0x7C000000u;
+}
+__device__ __forceinline__ void note_overflow(uint32_t *flag, bool bad, uint32_t bit) {
+  if (flag && bad) atomicOr(flag, bit);
+}
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 // ------------------------------------------------------------------ routing
@@ -46,6 +57,7 @@ struct TopkArgs {
   const uint16_t *x;        // bf16 [T][d]
   uint16_t *x16;            // fp16 [T][d], each 8-element run stored as 0,4,1,5,2,6,3,7
   int d;
+  uint32_t *overflow;       // nullable: MOE_OVERFLOW_X when an x16 value is not finite
 };
 
 // y[t] = sum_j w[t][j] * o[pair_pos[t*k+j]] + o_sh[t], slot order, fp32.
@@ -116,6 +128,7 @@ struct GemmProblem {
   // outputs
   float *C; int ldc;          // kStoreC
   uint16_t *H; int ldh;       // kSwiGLU (permuted-run columns), kStoreH (natural columns)
+  uint32_t *overflow;         // nullable: MOE_OVERFLOW_H / _O when a stored fp16 value is out of range
 };
 
 struct GemmArgs {
@@ -154,6 +167,7 @@ struct DecodeArgs {
   uint16_t *h;                // fp16 [T][k+1][fmax] (slot k: shared expert); within each
                               // 8 columns, the rebuild order 0,4,1,5,2,6,3,7
   float *y;                   // fp32 [T][d]
+  uint32_t *overflow;         // nullable: MOE_OVERFLOW_X / _H bits
 };
 
 bool decode_supported(int T, const moe_layer_t *L);

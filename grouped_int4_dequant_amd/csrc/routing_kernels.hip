@@ -65,7 +65,8 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t two_bf16) {
          ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
 }
 
-template <int VPL>
+// CHECK: report x values that do not convert to a finite fp16.
+template <int VPL, bool CHECK>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x % kWave;
   const int gwave = blockIdx.x * kWaves + threadIdx.x / kWave;
@@ -98,6 +99,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         const uint32_t p2 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].w, v[u].y, 0x05040100u));  // (e2,e6)
         const uint32_t p3 = bf16x2_to_f16x2(__builtin_amdgcn_perm(v[u].w, v[u].y, 0x07060302u));  // (e3,e7)
         reinterpret_cast<uint4 *>(a.x16)[i] = make_uint4(p0, p1, p2, p3);
+        if (CHECK)
+          note_overflow(a.overflow, f16x2_nonfinite(p0) || f16x2_nonfinite(p1) || f16x2_nonfinite(p2) ||
+                                        f16x2_nonfinite(p3), MOE_OVERFLOW_X);
       }
     }
     if (i0 + kUnroll * stride < n8) {
@@ -358,11 +362,19 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEv
   if (a.x16) nwg = (int)std::max<int64_t>(nwg, std::min<int64_t>(1024, ceil_div((int64_t)a.T * a.d / 8, 4 * kThreads)));
   nwg = std::min(nwg, 4096);
   const dim3 grid(nwg), block(kThreads);
-  if (vpl <= 1)       hipExtLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, start, stop, 0, a);
-  else if (vpl <= 2)  hipExtLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, start, stop, 0, a);
-  else if (vpl <= 4)  hipExtLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, start, stop, 0, a);
-  else if (vpl <= 8)  hipExtLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, start, stop, 0, a);
-  else                hipExtLaunchKernelGGL(topk_kernel<kMaxVpl>, grid, block, 0, s, start, stop, 0, a);
+  if (a.overflow) {
+    if (vpl <= 1)       hipExtLaunchKernelGGL((topk_kernel<1, true>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 2)  hipExtLaunchKernelGGL((topk_kernel<2, true>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 4)  hipExtLaunchKernelGGL((topk_kernel<4, true>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 8)  hipExtLaunchKernelGGL((topk_kernel<8, true>), grid, block, 0, s, start, stop, 0, a);
+    else                hipExtLaunchKernelGGL((topk_kernel<kMaxVpl, true>), grid, block, 0, s, start, stop, 0, a);
+  } else {
+    if (vpl <= 1)       hipExtLaunchKernelGGL((topk_kernel<1, false>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 2)  hipExtLaunchKernelGGL((topk_kernel<2, false>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 4)  hipExtLaunchKernelGGL((topk_kernel<4, false>), grid, block, 0, s, start, stop, 0, a);
+    else if (vpl <= 8)  hipExtLaunchKernelGGL((topk_kernel<8, false>), grid, block, 0, s, start, stop, 0, a);
+    else                hipExtLaunchKernelGGL((topk_kernel<kMaxVpl, false>), grid, block, 0, s, start, stop, 0, a);
+  }
   return hipGetLastError();
 }
 

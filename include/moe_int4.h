@@ -270,6 +270,29 @@ int moe_layer_forward_noalloc(const moe_layer_t *L, const uint16_t *x, const flo
                               float *y, const moe_routing_t *routing, hipStream_t stream);
 
 /*
+ * moe_layer_forward with a check of the fp16 range. The path keeps x, the
+ * SwiGLU output h and each expert's output o in fp16 (the header's numerics
+ * note); a value outside fp16's finite range (magnitude 65520 or more, or
+ * NaN) becomes infinite or NaN there and reaches y. overflow: device pointer
+ * to one uint32 that the caller has set (usually to 0); the call ORs into it
+ *   MOE_OVERFLOW_X  an x value did not convert to a finite fp16
+ *   MOE_OVERFLOW_H  an h value was out of range
+ *   MOE_OVERFLOW_O  an expert output o was out of range (prefill form; the
+ *                   few-token form keeps o in fp32 and never sets it)
+ * and leaves it unchanged when every stored value is finite. overflow may be
+ * NULL (then this is moe_layer_forward). Values of |x| below 2^-17 lose low
+ * bits in fp16 (subnormal spacing 2^-24) without setting a bit: their
+ * products are far below the other terms' rounding. Other arguments and
+ * errors as moe_layer_forward.
+ */
+#define MOE_OVERFLOW_X 1u
+#define MOE_OVERFLOW_H 2u
+#define MOE_OVERFLOW_O 4u
+int moe_layer_forward_checked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
+                              float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                              hipStream_t stream, uint32_t *overflow);
+
+/*
  * moe_layer_forward with stage timing, for measurement. The events are
  * attached to the kernel dispatches themselves (no marker packets between
  * kernels, so timing adds no idle time): events[0] at the start of the top-k
