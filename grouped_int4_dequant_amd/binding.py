@@ -86,6 +86,11 @@ def load() -> ctypes.CDLL:
         lib.moe_layer_forward_checked.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
                                                   ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P, _P]
         lib.moe_layer_forward_checked.restype = ctypes.c_int
+        lib.moe_router_topk.argtypes = [_P, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _P]
+        lib.moe_router_topk.restype = ctypes.c_int
+        lib.moe_layer_forward_router.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
+                                                 ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P]
+        lib.moe_layer_forward_router.restype = ctypes.c_int
         lib.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         lib.moe_router_logits.restype = ctypes.c_int
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
@@ -319,6 +324,43 @@ def router_logits(x: torch.Tensor, w_r: torch.Tensor, logits: Optional[torch.Ten
     _check(load().moe_router_logits(x.data_ptr(), T, d, w_r.data_ptr(), E, logits.data_ptr(), _stream(stream)),
            "moe_router_logits")
     return logits
+
+
+def router_topk(x: torch.Tensor, w_r: torch.Tensor, k: int, logits: Optional[torch.Tensor] = None,
+                stream=None):
+    """moe_router_topk: (topk_ids int32 [T][k], topk_w fp32 [T][k]) from bf16
+    x [T][d] and bf16 W_r [E][d]; the fp32 logits [T][E] go to `logits`
+    (allocated when not given)."""
+    T, d = x.shape
+    E = w_r.shape[0]
+    _need(x, "x", torch.bfloat16, (T, d))
+    _need(w_r, "w_r", torch.bfloat16, (E, d))
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if logits is None else logits
+    _need(logits, "logits", torch.float32, (T, E))
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(load().moe_router_topk(x.data_ptr(), T, d, w_r.data_ptr(), E, k, _ptr(logits), ids.data_ptr(),
+                                  w.data_ptr(), _stream(stream)), "moe_router_topk")
+    return ids, w
+
+
+def layer_forward_router(layer: Layer, x: torch.Tensor, w_r: torch.Tensor,
+                         y: Optional[torch.Tensor] = None,
+                         routing: Optional[Dict[str, torch.Tensor]] = None,
+                         ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_layer_forward_router: the whole layer from bf16 router weights
+    W_r [E][d] instead of logits."""
+    T = x.shape[0]
+    _need(x, "x", torch.bfloat16, (T, layer.d))
+    _need(w_r, "w_r", torch.bfloat16, (layer.E, layer.d))
+    y = torch.empty((T, layer.d), dtype=torch.float32, device=x.device) if y is None else y
+    _need(y, "y", torch.float32, (T, layer.d))
+    ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load().moe_layer_forward_router(ctypes.byref(layer.c), x.data_ptr(), w_r.data_ptr(), T, y.data_ptr(),
+                                           ctypes.byref(rs) if rs is not None else None, ws.data_ptr(),
+                                           ws.numel(), _stream(stream)), "moe_layer_forward_router")
+    return y
 
 
 ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2, "unfused": 3}

@@ -110,6 +110,7 @@ struct Workspace {
   int32_t *chunk_counts;
   uint16_t *x16, *h, *h_sh, *o, *o_sh;
   uint16_t *dec_h;  // decode-shape calls only
+  float *logits;    // [T][E]: router logits of moe_layer_forward_router when they go through memory
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
@@ -135,6 +136,7 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w,
   o.units = c.take<int32_t>(3 * (size_t)max_units_routed(T, k, E, kMinUnitRows));  // any unit size
   o.num_units = c.take<int32_t>(1);
   o.chunk_counts = c.take<int32_t>((size_t)ceil_div(T, kSubChunk) * E);
+  o.logits = c.take<float>((size_t)T * E);
   o.x16 = c.take<uint16_t>((size_t)T * L->d);
   ofs.x16 = (int64_t)c.last;
   // The shared expert's rows follow the routed rows in h and o when their
@@ -174,12 +176,16 @@ size_t layer_ws_bytes(int T, const moe_layer_t *L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+int enqueue_scan(int T, int E, int k, const moe_routing_t &rt, int32_t *chunk_counts, int32_t *units,
+                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows);
+
 int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
                   int32_t *chunk_counts, int32_t *units, int32_t *num_units, const uint16_t *x,
                   uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr, int unit_rows = kUnitRows,
                   uint32_t *overflow = nullptr) {
+  hipError_t err;
   TopkArgs ta{};
   ta.overflow = overflow;
   ta.logits = logits;
@@ -191,9 +197,14 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   ta.x = x;
   ta.x16 = x16;
   ta.d = d;
-  hipError_t err = launch_topk(ta, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+  err = launch_topk(ta, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   if (err != hipSuccess) return MOE_EHIP;
+  return enqueue_scan(T, E, k, rt, chunk_counts, units, num_units, s, ev, unit_rows);
+}
 
+// Histogram, scan, stable scatter, block map and work list from rt.topk_ids.
+int enqueue_scan(int T, int E, int k, const moe_routing_t &rt, int32_t *chunk_counts, int32_t *units,
+                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows) {
   ScanArgs sa{};
   sa.T = T;
   sa.E = E;
@@ -308,7 +319,7 @@ int host_route(int T, int E, int k, int unit_rows, const moe_routing_t &rt, int3
 int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, int T, float *y,
                 const moe_routing_t *routing, void *ws, size_t ws_bytes, hipStream_t s,
                 hipEvent_t *ev = nullptr, const FwdOptions &opt = FwdOptions{kUnitRows, kNarrowTail, false, true},
-                uint32_t *overflow = nullptr) {
+                uint32_t *overflow = nullptr, const uint16_t *w_r = nullptr) {
   const size_t need = layer_ws_bytes(T, L);
   if (ws_bytes < need + (opt.unfused ? expand_bytes(L) : 0)) return MOE_EWORKSPACE;
   Workspace w;
@@ -324,7 +335,16 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     return MOE_EUNSUPPORTED;
 
   int st = MOE_OK;
-  if (opt.few_token_form && decode_supported(T, L)) {
+  const bool decode_form = opt.few_token_form && decode_supported(T, L);
+  if (w_r) {
+    // the router's logits go through the workspace; the layer then runs as usual
+    RouterArgs ra{};
+    ra.x = x; ra.w = w_r; ra.T = T; ra.d = d; ra.E = E; ra.logits = w.logits;
+    st = hip_status(launch_router(ra, s));
+    if (st != MOE_OK) return st;
+    logits = w.logits;
+  }
+  if (decode_form) {
     // A few tokens: gate/up (routing repeated inside) and down + combine.
     // Routing tensors are produced by the routing kernels only when asked for.
     if (routing) {
@@ -554,6 +574,40 @@ int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logi
   if (!x || !logits || !y || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
   return forward_one(L, x, logits, T, y, routing, ws, ws_bytes, stream);
+}
+
+int moe_router_topk(const uint16_t *x, int32_t T, int32_t d, const uint16_t *w_r, int32_t E, int32_t k,
+                    float *logits, int32_t *topk_ids, float *topk_w, hipStream_t stream) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (d % 32 || E > MOE_MAX_EXPERTS || k > kMaxTopK || T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_r || !logits || !topk_ids || !topk_w || !aligned16(x) || !aligned16(w_r) || !aligned16(logits))
+    return MOE_EINVAL;
+  RouterArgs ra{};
+  ra.x = x; ra.w = w_r; ra.T = T; ra.d = d; ra.E = E; ra.logits = logits;
+  int st = hip_status(launch_router(ra, stream));
+  if (st != MOE_OK) return st;
+  TopkArgs ta{};
+  ta.logits = logits; ta.T = T; ta.E = E; ta.k = k; ta.topk_ids = topk_ids; ta.topk_w = topk_w;
+  return hip_status(launch_topk(ta, stream));
+}
+
+int moe_layer_forward_router(const moe_layer_t *L, const uint16_t *x, const uint16_t *w_r, int32_t T,
+                             float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxRouteTokens || L->d % 32) return MOE_EUNSUPPORTED;
+  if (routing && check_routing(routing) != MOE_OK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_r || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_r) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  // logits are computed into the workspace where needed; forward_one reads them from there
+  Workspace w;
+  carve_layer(T, L, static_cast<char *>(ws), &w);
+  return forward_one(L, x, w.logits, T, y, routing, ws, ws_bytes, stream, nullptr,
+                     FwdOptions{kUnitRows, kNarrowTail, false, true}, nullptr, w_r);
 }
 
 int moe_layer_forward_checked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,

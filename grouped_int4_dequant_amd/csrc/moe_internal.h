@@ -91,6 +91,7 @@ struct RouterArgs {
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 
+
 // Optional events (nullable) are attached to a kernel's dispatch: start at
 // its first wave, stop at its end, with no extra packet between kernels.
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start = nullptr,

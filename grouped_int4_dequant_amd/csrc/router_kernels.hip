@@ -10,7 +10,11 @@
 // per workgroup in chunks of 256 inputs (double buffered, 16-byte units
 // XOR-swizzled by row so the 16 rows read by one MFMA operand fetch hit
 // distinct banks); each wave reads its experts' weights straight from
-// memory, requesting the next chunk's before computing the current one.
+// memory, requesting the next chunk's before computing the current one. The
+// chunk loop body has no per-step branch (columns past d are staged as
+// zeros, which add exactly zero to accumulators that start at +0, and the
+// chunk count is rounded up to the unroll of two), so the compiler keeps the
+// next chunk's loads in flight across iterations.
 
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -39,7 +43,11 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   const int ec = min(e, a.E - 1);
   const uint4 *wr = reinterpret_cast<const uint4 *>(a.w + (int64_t)ec * a.d) + kq;
   const int steps = a.d / 32;                             // this lane's 16-byte chunk of step s is 4 s + kq
-  const int nchunks = (steps + kChunkSteps - 1) / kChunkSteps;
+  // chunks rounded up to an even count: the loop body is straight-line code
+  // (no per-step branch), so the compiler keeps the next chunk's loads in
+  // flight across the loop; columns past d are staged as zeros, which add
+  // exactly zero to accumulators that start at +0
+  const int nchunks = 2 * ((steps + 2 * kChunkSteps - 1) / (2 * kChunkSteps));
 
   // token-row staging: unit u = tid + 256 i of a chunk is row u / 32, 16-byte
   // column u % 32 (rows past T repeat the last token; columns past d are not
@@ -56,11 +64,14 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     return reinterpret_cast<uint4 *>(&s_x[buf][r * kRowBytes + 16 * (j ^ (r & 15))]);
   };
   uint4 x0, x1, x2, x3;  // this thread's four units of the next chunk
+  auto live = [&](int c, int i) { return c * kChunkSteps * 32 + 8 * ((tid + 256 * i) & 31) < a.d; };
   auto load_x = [&](int c) {
-    x0 = *x_src(c, 0);
-    x1 = *x_src(c, 1);
-    x2 = *x_src(c, 2);
-    x3 = *x_src(c, 3);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 v0 = *x_src(c, 0), v1 = *x_src(c, 1), v2 = *x_src(c, 2), v3 = *x_src(c, 3);
+    x0 = live(c, 0) ? v0 : z;
+    x1 = live(c, 1) ? v1 : z;
+    x2 = live(c, 2) ? v2 : z;
+    x3 = live(c, 3) ? v3 : z;
   };
   auto store_x = [&](int buf) {
     *x_dst(buf, 0) = x0;
@@ -86,14 +97,12 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     const uint8_t *xb = s_x[c & 1];
 #pragma unroll
     for (int u = 0; u < kChunkSteps; ++u) {
-      if (c * kChunkSteps + u < steps) {
-        const int j = 4 * u + kq;
-        const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
-        const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
-        const bf8 wv = __builtin_bit_cast(bf8, w[u]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), wv, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), wv, acc1, 0, 0, 0);
-      }
+      const int j = 4 * u + kq;
+      const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
+      const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
+      const bf8 wv = __builtin_bit_cast(bf8, w[u]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), wv, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), wv, acc1, 0, 0, 0);
     }
     store_x((c + 1) & 1);
   };
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   store_x(0);
   for (int c = 0; c < nchunks; c += 2) {
     body(c, w0, w1);
-    if (c + 1 < nchunks) body(c + 1, w1, w0);
+    body(c + 1, w1, w0);
   }
   // element i of lane (c16, kq): token row 4 kq + i of the block, expert c16
   if (e < a.E) {

@@ -126,8 +126,8 @@ int32_t moe_max_blocks(int32_t T, int32_t E, int32_t k);
 /*
  * Bytes of device workspace moe_layer_forward needs for T tokens of layer L
  * (routing scratch, the fp16 activation copy, the fp16 expert
- * intermediates and the fp16 expert outputs; about 102 MB at T=2048,
- * d=2048, f=512, E=256, k=8). Non-decreasing in T, so a workspace sized for
+ * intermediates, the fp16 expert outputs and room for the router's logits;
+ * about 105 MB at T=2048, d=2048, f=512, E=256, k=8). Non-decreasing in T, so a workspace sized for
  * T serves every call of fewer tokens.
  * moe_prefill_chunked needs moe_workspace_bytes(chunk, L). Host-only: reads
  * the scalar fields of L. Returns 0 when the arguments are invalid.
@@ -179,6 +179,33 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E);
  */
 int moe_router_logits(const uint16_t *x, int32_t T, int32_t d, const uint16_t *w_r, int32_t E,
                       float *logits, hipStream_t stream);
+
+/*
+ * Router projection followed by the top-k (Lily-EN "Three Workload Shapes": a
+ * router scores 256 experts and keeps 8): logits[t][e] = sum_k x[t][k] *
+ * w_r[e][k] exactly as moe_router_logits computes them (written to logits,
+ * fp32 [T][E], device), then topk_ids [T][k] and topk_w [T][k] exactly as
+ * moe_route derives them from those logits. Two kernels on the stream. x bf16
+ * [T][d], w_r bf16 [E][d] (16-byte aligned, d a multiple of 32).
+ * Errors: MOE_EINVAL (null or unaligned pointer, T < 0, d < 1, k < 1, k > E),
+ * MOE_EUNSUPPORTED (d % 32, E > MOE_MAX_EXPERTS, k > 64, T >
+ * MOE_MAX_CALL_TOKENS). T == 0 enqueues nothing.
+ */
+int moe_router_topk(const uint16_t *x, int32_t T, int32_t d, const uint16_t *w_r, int32_t E, int32_t k,
+                    float *logits, int32_t *topk_ids, float *topk_w, hipStream_t stream);
+
+/*
+ * The whole layer from the router weights instead of logits: the router
+ * projection (x w_r^T, as moe_router_logits) writes the logits into the
+ * workspace and the layer of moe_layer_forward runs on them, so the results
+ * equal moe_layer_forward's on moe_router_logits' output bit for bit.
+ * w_r bf16 [E][d], 16-byte aligned, d a multiple of 32. ws as
+ * moe_workspace_bytes(T, L), which covers this call. Other arguments and
+ * errors as moe_layer_forward.
+ */
+int moe_layer_forward_router(const moe_layer_t *L, const uint16_t *x, const uint16_t *w_r, int32_t T,
+                             float *y, const moe_routing_t *routing, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /*
  * Routing only. logits fp32 [T][E] (device). Fills every field of *out (the

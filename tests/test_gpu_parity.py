@@ -300,7 +300,7 @@ def _router_bound(x_bits, w_bits):
     return (d - 1) * 2.0 ** -24 * (np.abs(O.bf16_value(x_bits)) @ np.abs(O.bf16_value(w_bits)).T)
 
 
-@pytest.mark.parametrize("T,d,E", [(2048, 2048, 256), (37, 96, 20), (1, 32, 1), (130, 512, 1024)])
+@pytest.mark.parametrize("T,d,E", [(2048, 2048, 256), (37, 96, 20), (1, 32, 1), (130, 512, 1024), (45, 2080, 70)])
 def test_router_logits_match_oracle(moe, T, d, E):
     say(f"router T={T} d={d} E={E}")
     x, w = S.make_router_problem(T, d, E, seed=T + d + E)
@@ -394,3 +394,52 @@ def test_zero_tokens_is_a_noop(moe):
     y = torch.full((0, p.shape.d), 1.0, device="cuda")
     moe.layer_forward(layer, x[:0], lg[:0], y=y)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------ router fused with top-k
+@pytest.mark.parametrize("T,d,E,k", [(2048, 2048, 256, 8), (37, 96, 20, 3), (1, 64, 256, 8), (130, 512, 128, 8),
+                                     (64, 256, 16, 16), (70, 512, 300, 8), (45, 2080, 70, 4)])
+def test_router_topk_matches_own_logits(moe, T, d, E, k):
+    """moe_router_topk: its logits equal moe_router_logits' bit for bit, its
+    picks equal the oracle's top-k of those same fp32 logits bit for bit, its
+    gates the oracle's gates of them within 1e-6."""
+    say(f"router+topk T={T} d={d} E={E} k={k}")
+    x, w = S.make_router_problem(T, d, E, seed=T + d + E + k)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids, g = moe.router_topk(xt, wt, k, logits=lg)
+    ref_lg = moe.router_logits(xt, wt)
+    torch.cuda.synchronize()
+    L = lg.cpu().numpy()
+    assert np.array_equal(L, ref_lg.cpu().numpy()), "fused logits differ from moe_router_logits"
+    ref_ids = O.topk(L, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.max(np.abs(g.cpu().numpy().astype(np.float64) - O.gates(L, ref_ids))) <= 1e-6
+    err = np.abs(L.astype(np.float64) - O.router_logits(x, w))
+    assert np.all(err <= _router_bound(x, w))
+
+
+@pytest.mark.parametrize("T,E", [(2048, 256), (300, 64), (4, 256), (1, 256), (100, 300)])
+def test_layer_forward_router_equals_logits_path(moe, T, E):
+    """moe_layer_forward_router equals moe_layer_forward fed with
+    moe_router_logits' output, bit for bit, routing tensors included (prefill
+    and few-token forms); and it is within tolerance of the oracle on the
+    router's logits."""
+    shape = S.LayerShape(d=2048, f=512, E=E, k=8, f_sh=512)
+    p = S.make_custom(T, shape, seed=40 + T + E)
+    _, w = S.make_router_problem(1, 2048, E, seed=7 + E)
+    say(f"layer from router weights T={T} E={E}")
+    layer, x, _ = upload(p, moe)
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    r1 = moe.alloc_routing(T, E, 8)
+    r2 = moe.alloc_routing(T, E, 8)
+    y1 = moe.layer_forward_router(layer, x, wt, routing=r1)
+    lg = moe.router_logits(x, wt)
+    y2 = moe.layer_forward(layer, x, lg, routing=r2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), "layer from router weights differs from the logits path"
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+    if T <= 300:
+        check_output(y1.cpu().numpy(), O.moe_forward(p.layer, p.x, lg.cpu().numpy(), 8), f"router layer T={T} E={E}")
