@@ -104,6 +104,9 @@ def parse():
     ap.add_argument("--other-configs", type=int, default=1,
                     help="also time the 512-token layer and the skewed 8192-token prompt in 2048-token "
                          "chunks (0: skip)")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="also time the layer captured into a HIP graph at T=2048 and T=512: the one-stream "
+                         "capture and the concurrent capture (shared expert beside the routing) (0: skip)")
     ap.add_argument("--ablations", type=str, default="",
                     help="comma-separated token counts: also time the layer's ablation forms "
                          "(16-row work units; routing built on the host; weights expanded in memory "
@@ -248,6 +251,8 @@ def main():
         out["decode_t4"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events, T=4)
     if args.other_configs:
         out["other_configs"] = bench_prefill_configs(moe, S, torch, dev, args.steps)
+    if args.graph:
+        out["layer_graph"] = bench_graph(moe, S, torch, dev, args.steps)
     if args.ablations:
         out["ablations_us"] = bench_ablations(moe, lib, B, torch, layer, x, lg, y, ws, stream,
                                               [int(t) for t in args.ablations.split(",")],
@@ -326,6 +331,51 @@ def bench_prefill_configs(moe, S, torch, dev, steps):
                          "touched_experts_per_chunk": touched, "weight_bytes": wbytes,
                          "weight_gbps": wbytes / (us * 1e-6) / 1e9,
                          "hbm_frac": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del layer, x, lg, y, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_graph(moe, S, torch, dev, steps):
+    """GPU microseconds per call of the layer (configs 2 and 1) run eagerly,
+    as a one-stream HIP graph, and as the concurrent graph whose shared-expert
+    branch runs beside the routing (items of 96 and 48 rows), from events
+    around back-to-back calls; the forms alternate twice and the lower figure
+    of each is kept."""
+    res = {}
+    for ci in (2, 1):
+        p = S.make_problem(ci)
+        sh, T = p.shape, p.T
+        layer = moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, p.layer, device=dev)
+        x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        lg = torch.from_numpy(p.logits).to(dev)
+        y = torch.empty((T, sh.d), dtype=torch.float32, device=dev)
+        ws = moe.alloc_workspace(moe.workspace_bytes(T, layer), dev)
+        forms = {"eager": lambda: moe.layer_forward(layer, x, lg, y=y, ws=ws)}
+        graphs = {"graph_one_stream": moe.LayerGraph(layer, x, lg, y, ws=ws, concurrent=False),
+                  "graph_concurrent_96": moe.LayerGraph(layer, x, lg, y, ws=ws, concurrent=True,
+                                                        shared_unit_rows=96),
+                  "graph_concurrent_48": moe.LayerGraph(layer, x, lg, y, ws=ws, concurrent=True,
+                                                        shared_unit_rows=48)}
+        for name, g in graphs.items():
+            forms[name] = g.launch
+        best = {}
+        for _ in range(2):
+            for name, fn in forms.items():
+                for _ in range(5):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / steps
+                best[name] = min(us, best.get(name, us))
+        res[f"T{T}_us_per_call"] = best
+        for g in graphs.values():
+            g.close()
         del layer, x, lg, y, ws
         torch.cuda.empty_cache()
     return res

@@ -91,6 +91,13 @@ def load() -> ctypes.CDLL:
         lib.moe_layer_forward_router.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P,
                                                  ctypes.POINTER(MoeRoutingT), _P, ctypes.c_size_t, _P]
         lib.moe_layer_forward_router.restype = ctypes.c_int
+        lib.moe_layer_graph_create.argtypes = [ctypes.POINTER(MoeLayerT), _P, _P, _I32, _P, _P, ctypes.c_size_t,
+                                               _I32, _I32, _P, ctypes.POINTER(_P)]
+        lib.moe_layer_graph_create.restype = ctypes.c_int
+        lib.moe_layer_graph_launch.argtypes = [_P, _P]
+        lib.moe_layer_graph_launch.restype = ctypes.c_int
+        lib.moe_layer_graph_destroy.argtypes = [_P]
+        lib.moe_layer_graph_destroy.restype = ctypes.c_int
         lib.moe_router_logits.argtypes = [_P, _I32, _I32, _P, _I32, _P, _P]
         lib.moe_router_logits.restype = ctypes.c_int
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
@@ -361,6 +368,47 @@ def layer_forward_router(layer: Layer, x: torch.Tensor, w_r: torch.Tensor,
                                            ctypes.byref(rs) if rs is not None else None, ws.data_ptr(),
                                            ws.numel(), _stream(stream)), "moe_layer_forward_router")
     return y
+
+
+GRAPH_CONCURRENT = 1
+
+
+class LayerGraph:
+    """moe_layer_graph_create/_launch/_destroy: the layer captured once into a
+    HIP graph bound to x, logits, y and a workspace; launch() recomputes y
+    from their current contents. concurrent=True runs the shared expert on a
+    branch beside the routing (shared_unit_rows rows per item; 0: 96)."""
+
+    def __init__(self, layer: Layer, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
+                 ws: Optional[torch.Tensor] = None, concurrent: bool = True, shared_unit_rows: int = 0):
+        T = x.shape[0]
+        _need(x, "x", torch.bfloat16, (T, layer.d))
+        _need(logits, "logits", torch.float32, (T, layer.E))
+        _need(y, "y", torch.float32, (T, layer.d))
+        ws = alloc_workspace(workspace_bytes(T, layer), x.device) if ws is None else ws
+        self._keep = (layer, x, logits, y, ws)  # the graph holds their addresses
+        cap = torch.cuda.Stream(device=x.device)
+        cap.wait_stream(torch.cuda.current_stream(x.device))
+        h = ctypes.c_void_p()
+        _check(load().moe_layer_graph_create(ctypes.byref(layer.c), x.data_ptr(), logits.data_ptr(), T,
+                                             y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                             GRAPH_CONCURRENT if concurrent else 0, shared_unit_rows,
+                                             cap.cuda_stream, ctypes.byref(h)), "moe_layer_graph_create")
+        self._h = h.value
+
+    def launch(self, stream=None):
+        _check(load().moe_layer_graph_launch(self._h, _stream(stream)), "moe_layer_graph_launch")
+
+    def close(self):
+        if self._h:
+            _check(load().moe_layer_graph_destroy(self._h), "moe_layer_graph_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 ABLATIONS = {"none": 0, "tile16": 1, "host_routing": 2, "unfused": 3}

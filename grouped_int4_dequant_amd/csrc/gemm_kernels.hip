@@ -650,6 +650,10 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, h
         break;
       default: hipExtLaunchKernelGGL((gemm_kernel<kStoreC, true, false>), grid, block, 0, s, start, stop, 0, a); break;
     }
+  } else if (mode == kSwiGLU) {
+    // bf16 activations converted while staged: the shared expert's gate/up
+    // beside the routing (concurrent graph form)
+    hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, false, false>), grid, block, 0, s, start, stop, 0, a);
   } else {
     // bf16 activations: stand-alone GEMM over block-map entries (<= 32 rows)
     hipExtLaunchKernelGGL((gemm_kernel<kStoreC, false, false>), grid, block, 0, s, start, stop, 0, a);

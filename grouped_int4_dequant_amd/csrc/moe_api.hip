@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 #include <vector>
 
 using namespace moe;
@@ -67,6 +68,12 @@ struct FwdOptions {
   bool host_routing = false;  // counts, offsets, scatter, block map and work list built on the host
   bool few_token_form = true; // calls of at most 8 tokens take the two-kernel decode form
   bool unfused = false;       // weights expanded to fp16 in the workspace, then read by the GEMMs
+  // Concurrent form (graph capture): the shared expert's gate/up (from bf16
+  // x) and down run on `side`, forked from the main stream before routing
+  // and joined before the combine; `shared_unit_rows` rows per item there.
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int shared_unit_rows = kUnitRows;
 };
 
 // Unfused ablation: fp16 buffer for one projection's expanded weights (all
@@ -369,6 +376,40 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     return hip_status(launch_decode(a, s, gu_start, ev ? ev[3] : nullptr, ev ? ev[4] : nullptr));
   }
 
+  // concurrent form: the shared expert on the side stream, beside the routing
+  const bool split = opt.side != nullptr && fs > 0 && !opt.unfused;
+  if (split) {
+    if (hipEventRecord(opt.fork, s) != hipSuccess || hipStreamWaitEvent(opt.side, opt.fork, 0) != hipSuccess)
+      return MOE_EHIP;
+    GemmArgs gs{};
+    GemmProblem &p = gs.prob[0];
+    p.A = x; p.lda = d; p.a_row = nullptr;  // bf16 x, converted to fp16 while staged
+    p.Wq = L->sh_gu_q; p.Ws = L->sh_gu_s; p.Wb = L->sh_gu_b;
+    p.N = 2 * fs; p.K = d;
+    p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.shared_unit_rows;
+    p.nslices = (int)ceil_div(fs, kGemmCols / 2);
+    p.H = w.h_sh; p.ldh = fs;
+    p.overflow = overflow;
+    gs.nprob = 1;
+    gs.total_wg = problem_wgs(ceil_div(T, opt.shared_unit_rows), p.nslices);
+    st = hip_status(launch_gemm(gs, kSwiGLU, false, opt.side));
+    if (st != MOE_OK) return st;
+    GemmArgs gd{};
+    GemmProblem &q = gd.prob[0];
+    q.A = w.h_sh; q.lda = fs; q.a_row = nullptr;
+    q.Wq = L->sh_dn_q; q.Ws = L->sh_dn_s; q.Wb = L->sh_dn_b;
+    q.N = d; q.K = fs;
+    q.units = nullptr; q.num_units = nullptr; q.implicit_rows = T; q.unit_rows = opt.shared_unit_rows;
+    q.nslices = (int)ceil_div(d, kGemmCols);
+    q.H = w.o_sh; q.ldh = d;
+    q.overflow = overflow;
+    gd.nprob = 1;
+    gd.total_wg = problem_wgs(ceil_div(T, opt.shared_unit_rows), q.nslices);
+    st = hip_status(launch_gemm(gd, kStoreH, true, opt.side));
+    if (st != MOE_OK) return st;
+    if (hipEventRecord(opt.join, opt.side) != hipSuccess) return MOE_EHIP;
+  }
+
   if (opt.host_routing) {
     TopkArgs ta{};
     ta.logits = logits; ta.T = T; ta.E = E; ta.k = k;
@@ -395,7 +436,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   }
   GemmArgs g1{};
   int nwg = 0, np = 0;
-  if (fs > 0) {
+  if (fs > 0 && !split) {
     GemmProblem &p = g1.prob[np++];
     p.A = w.x16; p.lda = d; p.a_row = nullptr;
     p.Wq = L->sh_gu_q; p.Ws = L->sh_gu_s; p.Wb = L->sh_gu_b;
@@ -441,7 +482,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   GemmArgs g2{};
   nwg = 0;
   np = 0;
-  if (fs > 0) {
+  if (fs > 0 && !split) {
     GemmProblem &p = g2.prob[np++];
     p.A = w.h_sh; p.lda = fs; p.a_row = nullptr;
     p.Wq = L->sh_dn_q; p.Ws = L->sh_dn_s; p.Wb = L->sh_dn_b;
@@ -475,6 +516,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   g2.total_wg = nwg;
   st = hip_status(launch_gemm(g2, kStoreH, true, s, nullptr, nullptr, opt.unfused));
   if (st != MOE_OK) return st;
+  if (split && hipStreamWaitEvent(s, opt.join, 0) != hipSuccess) return MOE_EHIP;
 
   return enqueue_combine(T, d, k, w.o, fs > 0 ? w.o_sh : nullptr, rt, y, s, ev);
 }
@@ -740,6 +782,88 @@ int moe_layer_forward_noalloc(const moe_layer_t *L, const uint16_t *x, const flo
   void *ws = device_scratch(dev);
   if (!ws) return MOE_EHIP;
   return forward_one(L, x, logits, T, y, routing, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
+// A captured layer call: the executable graph and the side stream and events
+// its concurrent form was captured with.
+struct moe_layer_graph {
+  hipGraphExec_t exec = nullptr;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+namespace {
+void destroy_graph(moe_layer_graph_t *g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->fork) (void)hipEventDestroy(g->fork);
+  if (g->join) (void)hipEventDestroy(g->join);
+  if (g->side) (void)hipStreamDestroy(g->side);
+  delete g;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_graph_create(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T, float *y,
+                           void *ws, size_t ws_bytes, int32_t flags, int32_t shared_unit_rows, hipStream_t stream,
+                           moe_layer_graph_t **out) {
+  if (!out) return MOE_EINVAL;
+  *out = nullptr;
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || !stream || (flags & ~MOE_GRAPH_CONCURRENT)) return MOE_EINVAL;
+  if (shared_unit_rows == 0) shared_unit_rows = kUnitRows;
+  if (shared_unit_rows < 16 || shared_unit_rows > kUnitRows || shared_unit_rows % 16) return MOE_EINVAL;
+  if (T > kMaxRouteTokens) return MOE_EUNSUPPORTED;
+  if (!x || !logits || !y || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws % kAlign)) return MOE_EINVAL;
+  if (ws_bytes < layer_ws_bytes(T, L)) return MOE_EWORKSPACE;
+  moe_layer_graph_t *g = new (std::nothrow) moe_layer_graph_t();
+  if (!g) return MOE_EHIP;
+  FwdOptions opt{kUnitRows, kNarrowTail, false, true};
+  if (flags & MOE_GRAPH_CONCURRENT) {
+    // default-priority side stream; events only order work
+    if (hipStreamCreateWithFlags(&g->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&g->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&g->join, hipEventDisableTiming) != hipSuccess) {
+      destroy_graph(g);
+      return MOE_EHIP;
+    }
+    opt.side = g->side;
+    opt.fork = g->fork;
+    opt.join = g->join;
+    opt.shared_unit_rows = shared_unit_rows;
+  }
+  hipGraph_t graph = nullptr;
+  if (hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    destroy_graph(g);
+    return MOE_EHIP;
+  }
+  st = forward_one(L, x, logits, T, y, nullptr, ws, ws_bytes, stream, nullptr, opt);
+  const hipError_t end = hipStreamEndCapture(stream, &graph);
+  if (st == MOE_OK && (end != hipSuccess || !graph)) st = MOE_EHIP;
+  if (st == MOE_OK && hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0) != hipSuccess) st = MOE_EHIP;
+  if (graph) (void)hipGraphDestroy(graph);
+  if (st != MOE_OK) {
+    destroy_graph(g);
+    return st;
+  }
+  *out = g;
+  return MOE_OK;
+}
+
+int moe_layer_graph_launch(moe_layer_graph_t *g, hipStream_t stream) {
+  if (!g || !g->exec) return MOE_EINVAL;
+  return hip_status(hipGraphLaunch(g->exec, stream));
+}
+
+int moe_layer_graph_destroy(moe_layer_graph_t *g) {
+  if (!g) return MOE_EINVAL;
+  destroy_graph(g);
+  return MOE_OK;
 }
 
 const char *moe_status_string(int status) {

@@ -383,6 +383,38 @@ int moe_layer_forward_ablation(const moe_layer_t *L, const uint16_t *x, const fl
 int moe_prefill_chunked(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,
                         int32_t chunk, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * A layer call captured once into a HIP graph and launched many times
+ * (Lily-EN "Decode: Minimize Bytes Moved Per Token": a recorded pass whose
+ * real dependencies let independent kernels overlap). The graph is bound to
+ * the given x, logits, y and workspace: each launch recomputes y from their
+ * current contents, with results equal bit for bit to moe_layer_forward's.
+ * flags:
+ *   MOE_GRAPH_CONCURRENT  prefill form with a shared expert: its gate/up
+ *                         (reading bf16 x directly) and down run on a
+ *                         branch beside the routing kernels and the routed
+ *                         GEMMs, joined before the combine; items of
+ *                         shared_unit_rows rows (16..96, multiple of 16; 0
+ *                         means 96). Without the flag the capture is the
+ *                         one-stream sequence of moe_layer_forward.
+ * stream: a non-default stream to capture on (the capture is thread-local);
+ * nothing is executed while capturing. The graph holds a side stream and two
+ * events (allocated here, released by moe_layer_graph_destroy). Calls that
+ * launch the same graph, or share its workspace, must be ordered.
+ * Errors: MOE_EINVAL (as moe_layer_forward, T < 1, a null stream or out,
+ * unknown flags, bad shared_unit_rows), MOE_EUNSUPPORTED, MOE_EWORKSPACE,
+ * MOE_EHIP (stream, event or graph creation failed).
+ */
+#define MOE_GRAPH_CONCURRENT 1
+typedef struct moe_layer_graph moe_layer_graph_t;
+int moe_layer_graph_create(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T, float *y,
+                           void *ws, size_t ws_bytes, int32_t flags, int32_t shared_unit_rows,
+                           hipStream_t stream, moe_layer_graph_t **graph);
+/* Enqueue one run of the captured layer on stream. */
+int moe_layer_graph_launch(moe_layer_graph_t *graph, hipStream_t stream);
+/* Release the graph and what it holds (after its launches have completed). */
+int moe_layer_graph_destroy(moe_layer_graph_t *graph);
+
 /* Static description of a status code. Never NULL. */
 const char *moe_status_string(int status);
 
