@@ -22,7 +22,9 @@
 //   * Each group's scale and bias are read once per work unit with coalesced
 //     loads into an LDS table of fp16 (s, b + 8s) pairs.
 //   * Weights go HBM -> VGPR with one 128-bit load per lane and column block
-//     per K step, one step ahead of use, and are rebuilt in registers:
+//     per K step, one step ahead of use (buffer loads whose per-step offset
+//     sits in a scalar register when K is a multiple of the step, so stepping
+//     costs no per-lane address arithmetic), and are rebuilt in registers:
 //     v_and_or_b32 puts two codes into fp16 "1024+v" slots, v_pk_add_f16
 //     removes the offset exactly, v_pk_fma_f16 applies the group scale and
 //     bias: w = fp16(s*(q-8) + (b+8s)). Only registers hold the rebuilt tile.
@@ -108,6 +110,19 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
   return r;
 }
 
+// Raw buffer resource over memory from base on, with no range limit (every
+// access made through it is in bounds by construction). Loads through it
+// take the per-step K offset as the instruction's scalar offset, so a K step
+// costs no per-lane address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Workgroup barrier that first drains this wave's LDS operations. The memory
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -132,7 +147,11 @@ struct Unit {
 // NRB = 16-row MFMA blocks of the unit (1..6), fixed at compile time so a K
 // step is one branch-free block the compiler can schedule as a whole.
 // CHECK: report fp16 values out of range through P.overflow (epilogues).
-template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB>
+// BUF: K is a multiple of the 128-input step (and the activations are fp16):
+// the K loop's loads are buffer loads with the step offset in a scalar
+// register; otherwise per-lane clamped addresses keep the last step's
+// quarters past K on their row.
+template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB, bool BUF>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
   constexpr int kMaxRB = NRB;
@@ -199,7 +218,20 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // first input of this lane's quarter at step s (valid iff < K)
   auto lane_k0 = [&](int s) { return kKStep * s + 32 * kq; };
 
+  // BUF (K a multiple of the step, so no lane ever reads past K): codes by
+  // buffer loads at lane offset 4 b_row + 16 kq bytes and step offset 64 s
+  // bytes.
+  const __amdgpu_buffer_rsrc_t rsrc_b = raw_rsrc(wq);
+  uint32_t b_voff[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) b_voff[cb] = 4u * b_row[cb] + 16u * (uint32_t)kq;
   auto load_b = [&](Stage &st, int s) {
+    if constexpr (BUF) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        st.q[cb] = __builtin_bit_cast(u4, buf_load16(rsrc_b, b_voff[cb], 64u * (uint32_t)s));
+      return;
+    }
     const int k0 = lane_k0(s);
     const int kc = k0 < K ? k0 : 0;
     if constexpr (WX) {
@@ -294,7 +326,18 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   };
 
   uint4 a_regs[kSlabs];
+  // BUF: fp16 activations by buffer loads at lane offset = the byte offset
+  // of its row and chunk, step offset 256 s bytes.
+  const __amdgpu_buffer_rsrc_t rsrc_a = raw_rsrc(P.A);
+  uint32_t a_voff[kSlabs];
+#pragma unroll
+  for (int ii = 0; ii < kSlabs; ++ii) a_voff[ii] = 2u * (uint32_t)(a_row_off[ii] + (AOff)a_in[ii]);
   auto load_a = [&](int s) {
+    if constexpr (BUF) {
+#pragma unroll
+      for (int ii = 0; ii < kSlabs; ++ii) a_regs[ii] = buf_load16(rsrc_a, a_voff[ii], 256u * (uint32_t)s);
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < kSlabs; ++ii)
       a_regs[ii] = *reinterpret_cast<const uint4 *>(a_src(s, ii));
@@ -544,6 +587,20 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   }
 }
 
+// The unit's 16-row block count picks the compiled form.
+template <int MODE, bool AF16, bool WX, bool CHECK, int CB, bool BUF>
+__device__ __forceinline__ void run_rows(const GemmProblem &P, const Unit &U, uint8_t *lds, const int *s_arow,
+                                         uint32_t *tab) {
+  switch ((U.nr + 15) >> 4) {
+    case 1: run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF>(P, U, lds, s_arow, tab); break;
+    case 2: run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF>(P, U, lds, s_arow, tab); break;
+    case 3: run_unit<MODE, AF16, WX, CHECK, 3, CB, BUF>(P, U, lds, s_arow, tab); break;
+    case 4: run_unit<MODE, AF16, WX, CHECK, 4, CB, BUF>(P, U, lds, s_arow, tab); break;
+    case 5: run_unit<MODE, AF16, WX, CHECK, 5, CB, BUF>(P, U, lds, s_arow, tab); break;
+    default: run_unit<MODE, AF16, WX, CHECK, 6, CB, BUF>(P, U, lds, s_arow, tab); break;
+  }
+}
+
 template <int MODE, bool AF16, bool WX, bool CHECK = false>
 __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
@@ -601,24 +658,14 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
 
   // half-width items: the same code with half the column blocks per wave
   // (always, for expanded weights: their stages take four times the registers)
+  constexpr bool kCanBuf = AF16 && !WX;
+  const bool buf = kCanBuf && (P.K & (kKStep - 1)) == 0;
   if (WX || narrow) {
-    switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, WX, CHECK, 1, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, WX, CHECK, 2, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, WX, CHECK, 3, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, WX, CHECK, 4, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, WX, CHECK, 5, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, WX, CHECK, 6, kCBFull / 2>(P, U, lds, s_arow, tab); break;
-    }
+    if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf>(P, U, lds, s_arow, tab);
+    else     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, false>(P, U, lds, s_arow, tab);
   } else {
-    switch ((U.nr + 15) >> 4) {
-      case 1: run_unit<MODE, AF16, WX, CHECK, 1, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 2: run_unit<MODE, AF16, WX, CHECK, 2, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 3: run_unit<MODE, AF16, WX, CHECK, 3, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 4: run_unit<MODE, AF16, WX, CHECK, 4, kCBFull>(P, U, lds, s_arow, tab); break;
-      case 5: run_unit<MODE, AF16, WX, CHECK, 5, kCBFull>(P, U, lds, s_arow, tab); break;
-      default: run_unit<MODE, AF16, WX, CHECK, 6, kCBFull>(P, U, lds, s_arow, tab); break;
-    }
+    if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf>(P, U, lds, s_arow, tab);
+    else     run_rows<MODE, AF16, WX, CHECK, kCBFull, false>(P, U, lds, s_arow, tab);
   }
 }
 

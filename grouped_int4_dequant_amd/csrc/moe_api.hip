@@ -335,10 +335,10 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   const moe_routing_t &rt = routing ? *routing : w.rt;
   const int d = L->d, f = L->f, E = L->E, k = L->k, fs = L->f_sh;
   // The GEMM addresses the layer's fp16 activation buffers and one expert's
-  // codes with 32-bit offsets.
+  // codes with 32-bit byte offsets.
   const int64_t wmax = std::max<int64_t>(f, fs);
   if ((int64_t)T * (k + 1) * wmax >= (1LL << 31) || (int64_t)T * d >= (1LL << 31) ||
-      2 * wmax * d / 8 >= (1LL << 31))
+      2 * wmax * d / 8 >= (1LL << 30))
     return MOE_EUNSUPPORTED;
 
   int st = MOE_OK;

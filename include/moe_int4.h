@@ -263,7 +263,7 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
  * Errors: MOE_EINVAL (null or misaligned pointer, T < 0, k > E),
  * MOE_EUNSUPPORTED (E > 1024, k > 64, d/f/f_sh not multiples of 64,
  * T > MOE_MAX_CALL_TOKENS, or a layer so large that T * (k + 1) * max(f, f_sh),
- * T * d or one expert's 2 * max(f, f_sh) * d / 8 code words reach 2^31),
+ * T * d reach 2^31 or one expert's 2 * max(f, f_sh) * d / 8 code words 2^30),
  * MOE_EWORKSPACE, MOE_EHIP.
  */
 int moe_layer_forward(const moe_layer_t *L, const uint16_t *x, const float *logits, int32_t T,

@@ -65,6 +65,7 @@ def test_status_strings():
     ("f", 500, B.MOE_EUNSUPPORTED),
     ("f_sh", 100, B.MOE_EUNSUPPORTED),
     ("E", 2048, B.MOE_EUNSUPPORTED),
+    ("f", 1 << 21, B.MOE_EUNSUPPORTED),   # one expert's gate/up codes: 2^30 words (4 GiB), past 32-bit byte offsets
     ("k", 300, B.MOE_EINVAL),
     ("k", 0, B.MOE_EINVAL),
     ("gu_q", None, B.MOE_EINVAL),
