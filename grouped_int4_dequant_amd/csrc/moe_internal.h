@@ -79,7 +79,8 @@ struct ScanArgs {
   int32_t *units, *num_units;   // optional GEMM work list (nullptr: none)
   int max_units;
   int unit_rows;                // rows per GEMM work unit at most (16..kUnitRows)
-  int32_t *chunk_counts;        // scratch [ceil(T/64)][E]
+  int32_t *chunk_counts;        // scratch [ceil(T/64)][E] (two-pass form only)
+  int count_inline;             // set by launch_scan: the scatter workgroups count every pair themselves
 };
 
 // logits[t][e] = sum_k x[t][k] * w[e][k] (bf16 inputs, fp32 accumulation).

@@ -4,8 +4,8 @@
 // map inside one GPU command buffer so no CPU synchronisation happens inside
 // an MoE layer (Lily-EN "Prefill: Keep Weights Packed, Keep Routing on the
 // GPU"; Lily-ES "Precarga: mantenga los pesos empaquetados, siga enrutando en
-// la GPU"). Here that is two kernels on one stream whose grids depend only on
-// T, never on routed counts:
+// la GPU"). Here that is two kernels on one stream (three above 32768
+// pairs) whose grids depend only on T, never on routed counts:
 //
 //   topk  one wave per token. Every candidate becomes a 64-bit key
 //         (order-preserving logit bits, then the inverted expert index), so
@@ -15,12 +15,13 @@
 //         across rows, the logit half first, then the index half) pick the
 //         experts; the gates are the softmax over the k picked logits. The
 //         same workgroups then convert x to fp16 for the GEMMs.
-//   count one workgroup per 64-token sub-chunk c: per-expert counts of its
-//         pairs, cnt[c][e].
-//   scatter one workgroup per sub-chunk: column sums of cnt give the expert
-//         totals and the counts before its sub-chunk, an exclusive scan over
-//         experts gives the offsets, and a 64-bit token mask per expert for
-//         its own sub-chunk gives the stable scatter:
+//   scatter one workgroup per 64-token sub-chunk c: the expert totals and
+//         the counts of the pairs before c (up to 32768 pairs each workgroup
+//         counts every pair itself in LDS; above that a count pass of one
+//         workgroup per sub-chunk writes cnt[c][e] first and the scatter
+//         takes column sums of it), an exclusive scan over experts gives the
+//         offsets, and a 64-bit token mask per expert for its own sub-chunk
+//         gives the stable scatter:
 //           pos = offset[e] + before[e] + popcount(mask[e] & tokens below t).
 //         Integer atomics commute, so the result is deterministic.
 //         One more workgroup writes counts, offsets, the 32-row block map and
@@ -46,6 +47,10 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxVpl = MOE_MAX_EXPERTS / kWave;  // logits per lane at E = 1024
 constexpr int kClasses = kUnitRows / 16;           // GEMM unit size classes (16-row blocks)
+// Up to this many (token, slot) pairs every scatter workgroup counts all of
+// them itself (each reads T*k ids, from L2); above it a count pass writes
+// per-sub-chunk counts first.
+constexpr int64_t kInlinePairs = 32768;
 
 template <int VPL>
 __device__ void route_token(const TopkArgs &a, int t, int lane) {
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void count_kernel(ScanArgs a) {
 }
 
 // Per sub-chunk c: expert totals and the counts of the sub-chunks before c
-// (column sums of cnt), offsets by an exclusive scan over experts, and the
+// (counted here, or column sums of cnt), offsets by an exclusive scan over experts, and the
 // stable scatter of c's pairs:
 //   pos = offset[e] + before[e] + popcount(mask[e] & tokens of c below t).
 // One extra workgroup (the last, with no pairs of its own) writes counts,
@@ -248,22 +253,51 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
     return u < kIdCache ? id : a.topk_ids[idx];
   };
 
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    int tot = 0, pre = 0;
-    for (int c0 = 0; c0 < C; c0 += 16) {  // sixteen independent loads in flight
-      int v[16];
+  if (a.count_inline) {
+    // Up to kInlinePairs pairs: the workgroup counts every pair itself, those
+    // before its sub-chunk into s_pre and the rest into s_aux (free until the
+    // block map), thirty-two id loads per thread in flight at a time.
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      s_pre[e] = 0;
+      s_aux[e] = 0;
+      s_mask[e] = 0ull;
+    }
+    __syncthreads();
+    constexpr int kBatch = 32;
+    for (int64_t b0 = threadIdx.x; b0 < tk; b0 += (int64_t)kBatch * kThreads) {
+      int v[kBatch];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = a.chunk_counts[(int64_t)min(c0 + u, C - 1) * E + e];
+      for (int u = 0; u < kBatch; ++u) v[u] = a.topk_ids[min(b0 + (int64_t)u * kThreads, tk - 1)];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        tot += c0 + u < C ? v[u] : 0;
-        pre += c0 + u < c ? v[u] : 0;
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t idx = b0 + (int64_t)u * kThreads;
+        if (idx < tk) atomicAdd(idx < lo ? &s_pre[v[u]] : &s_aux[v[u]], 1);
       }
     }
-    s_tot[e] = tot;
-    s_pre[e] = pre;
-    s_off[e] = tot;
-    s_mask[e] = 0ull;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      const int tot = s_pre[e] + s_aux[e];
+      s_tot[e] = tot;
+      s_off[e] = tot;
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      int tot = 0, pre = 0;
+      for (int c0 = 0; c0 < C; c0 += 16) {  // sixteen independent loads in flight
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = a.chunk_counts[(int64_t)min(c0 + u, C - 1) * E + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          tot += c0 + u < C ? v[u] : 0;
+          pre += c0 + u < c ? v[u] : 0;
+        }
+      }
+      s_tot[e] = tot;
+      s_pre[e] = pre;
+      s_off[e] = tot;
+      s_mask[e] = 0ull;
+    }
   }
   __syncthreads();
   {
@@ -383,11 +417,15 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s, hipEvent_t stop) 
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s, hipEvent_t stop) {
+hipError_t launch_scan(const ScanArgs &args, hipStream_t s, hipEvent_t stop) {
+  ScanArgs a = args;
   const int C = (int)ceil_div(a.T, kSubChunk);
-  hipLaunchKernelGGL(count_kernel, dim3(C), dim3(kThreads), 0, s, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  a.count_inline = (int64_t)a.T * a.k <= kInlinePairs;
+  if (!a.count_inline) {
+    hipLaunchKernelGGL(count_kernel, dim3(C), dim3(kThreads), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   // one workgroup per sub-chunk, plus one for the block map and work list
   hipExtLaunchKernelGGL(scatter_kernel, dim3(C + 1), dim3(kThreads), 0, s, nullptr, stop, 0, a);
   return hipGetLastError();

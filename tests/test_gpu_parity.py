@@ -100,6 +100,11 @@ def _adversarial_cases():
     cases.append(("ragged", rng.standard_normal((1000, 256)).astype(np.float32), 8))
     # E not a multiple of 64
     cases.append(("E_odd", rng.standard_normal((300, 67)).astype(np.float32), 5))
+    # 32768 pairs: the largest call whose scatter workgroups count every pair
+    # themselves; one token more takes the per-sub-chunk count pass
+    cases.append(("pairs_32768", rng.standard_normal((4096, 256)).astype(np.float32), 8))
+    cases.append(("pairs_32776", rng.standard_normal((4097, 256)).astype(np.float32), 8))
+    cases.append(("pairs_49152_T16384", rng.standard_normal((16384, 64)).astype(np.float32), 3))
     return cases
 
 
