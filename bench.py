@@ -234,6 +234,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "moe_layer_prefill", "T": T, "d": sh.d, "f": sh.f, "E": sh.E, "k": sh.k,
                    "f_sh": sh.f_sh, "weights": "int4 groupwise-affine g=64 bf16 scale+bias",
+                   "weights_layout": "prepared" if layer.c.prep else "original",
                    "inputs": "seeded synthetic (config 2 recipe)"},
         # achieved/frac/traffic: the dominant kernel (the contract's figure);
         # "layer": the whole call's useful FLOPs over its time per step, the
@@ -439,7 +440,7 @@ def bench_decode(moe, lib, B, S, torch, dev, stream, nsteps, make_events, T=1):
     cfg = S.CONFIGS[4]
     sh = cfg.shape
     steps = list(S.decode_steps(T, steps=nsteps + 20))
-    layers = [moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, steps[0].layer, device=dev)
+    layers = [moe.Layer.from_numpy(sh.d, sh.f, sh.E, sh.k, sh.f_sh, steps[0].layer, device=dev, prepare=False)
               for _ in range(4)]
     xs = [torch.from_numpy(s.x.view(np.int16)).view(torch.bfloat16).to(dev) for s in steps]
     lgs = [torch.from_numpy(s.logits).to(dev) for s in steps]

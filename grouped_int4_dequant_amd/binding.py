@@ -31,7 +31,8 @@ class MoeLayerT(ctypes.Structure):
                 ("gu_q", _P), ("gu_s", _P), ("gu_b", _P),
                 ("dn_q", _P), ("dn_s", _P), ("dn_b", _P),
                 ("sh_gu_q", _P), ("sh_gu_s", _P), ("sh_gu_b", _P),
-                ("sh_dn_q", _P), ("sh_dn_s", _P), ("sh_dn_b", _P)]
+                ("sh_dn_q", _P), ("sh_dn_s", _P), ("sh_dn_b", _P),
+                ("prep", _P)]
 
 
 class MoeRoutingT(ctypes.Structure):
@@ -103,6 +104,10 @@ def load() -> ctypes.CDLL:
         lib.moe_ablation_workspace_bytes.argtypes = [_I32, ctypes.POINTER(MoeLayerT), _I32]
         lib.moe_ablation_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_prefill_chunked.restype = ctypes.c_int
+        lib.moe_prepared_bytes.argtypes = [ctypes.POINTER(MoeLayerT)]
+        lib.moe_prepared_bytes.restype = ctypes.c_size_t
+        lib.moe_prepare_weights.argtypes = [ctypes.POINTER(MoeLayerT), _P, ctypes.c_size_t, _P]
+        lib.moe_prepare_weights.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -146,7 +151,8 @@ class Layer:
     KEYS = ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b",
             "sh_gu_q", "sh_gu_s", "sh_gu_b", "sh_dn_q", "sh_dn_s", "sh_dn_b")
 
-    def __init__(self, d: int, f: int, E: int, k: int, f_sh: int, tensors: Dict[str, torch.Tensor]):
+    def __init__(self, d: int, f: int, E: int, k: int, f_sh: int, tensors: Dict[str, torch.Tensor],
+                 prepare: bool = True):
         self.d, self.f, self.E, self.k, self.f_sh = d, f, E, k, f_sh
         self.tensors = dict(tensors)
         shapes = {"gu_q": (E, 2 * f, d // 8), "gu_s": (E, 2 * f, d // 64), "gu_b": (E, 2 * f, d // 64),
@@ -162,11 +168,30 @@ class Layer:
             t = self.tensors[key]
             _need(t, key, torch.int32 if key.endswith("_q") else torch.bfloat16, shapes[key])
             ptrs[key] = t.data_ptr()
-        self.c = MoeLayerT(d, f, E, k, f_sh, *[ptrs[k_] for k_ in self.KEYS])
+        self.c = MoeLayerT(d, f, E, k, f_sh, *[ptrs[k_] for k_ in self.KEYS], None)
+        self.prep = None
+        if prepare:
+            self.prepare()
+
+    def prepare(self, stream=None) -> bool:
+        """moe_prepare_weights into a new device buffer, then point c.prep at
+        it. Returns False (and leaves c.prep null) when the layer's shape has
+        no prepared form (d, f or f_sh not a multiple of 128)."""
+        lib = load()
+        n = int(lib.moe_prepared_bytes(ctypes.byref(self.c)))
+        if n == 0:
+            return False
+        dev = self.tensors["gu_q"].device
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        ptr = (buf.data_ptr() + 255) // 256 * 256
+        _check(lib.moe_prepare_weights(ctypes.byref(self.c), ptr, n, _stream(stream)), "moe_prepare_weights")
+        self.prep, self.c.prep = buf, ptr
+        return True
 
     @classmethod
-    def from_numpy(cls, d, f, E, k, f_sh, arrays, device="cuda"):
-        """Upload generator arrays (uint32 codes, uint16 bf16 bits) to the GPU."""
+    def from_numpy(cls, d, f, E, k, f_sh, arrays, device="cuda", prepare: bool = True):
+        """Upload generator arrays (uint32 codes, uint16 bf16 bits) to the GPU
+        (and, with prepare, build the prepared copy the prefill GEMMs read)."""
         import numpy as np
         ts = {}
         for key, a in arrays.items():
@@ -174,11 +199,15 @@ class Layer:
                 ts[key] = torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device)
             else:
                 ts[key] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
-        return cls(d, f, E, k, f_sh, ts)
+        return cls(d, f, E, k, f_sh, ts, prepare=prepare)
 
 
 def max_blocks(T: int, E: int, k: int) -> int:
     return int(load().moe_max_blocks(T, E, k))
+
+
+def prepared_bytes(layer: Layer) -> int:
+    return int(load().moe_prepared_bytes(ctypes.byref(layer.c)))
 
 
 def workspace_bytes(T: int, layer: Layer) -> int:

@@ -51,6 +51,7 @@
 //            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
 
 #include "moe_internal.h"
+#include "prep_layout.h"
 #include "rebuild_device.h"
 
 #include <hip/hip_fp16.h>
@@ -94,22 +95,6 @@ struct XStage {
   u4 q[CB][4];
 };
 
-__device__ __forceinline__ uint32_t pack_scale_bias(uint32_t s_bits, uint32_t b_bits) {
-  // (fp16 s, fp16 (b + 8 s)): the per-group constants of the rebuilt weight
-  const float sf = __uint_as_float(s_bits << 16), bf = __uint_as_float(b_bits << 16);
-  const uint32_t lo = __half_as_ushort(__float2half_rn(sf));
-  const uint32_t hi = __half_as_ushort(__float2half_rn(bf + 8.f * sf));
-  return lo | (hi << 16);
-}
-
-// A VGPR holding a constant, so v_and_or_b32 can take the mask from a VGPR
-// and the fp16 magic from an SGPR (VOP3 on gfx9 takes no literal).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
 // Raw buffer resource over memory from base on, with no range limit (every
 // access made through it is in bounds by construction). Loads through it
 // take the per-step K offset as the instruction's scalar offset, so a K step
@@ -151,7 +136,10 @@ struct Unit {
 // the K loop's loads are buffer loads with the step offset in a scalar
 // register; otherwise per-lane clamped addresses keep the last step's
 // quarters past K on their row.
-template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB, bool BUF>
+// PREP (implies BUF): codes and the scale/bias table come from the prepared
+// copy (prep_layout.h): every K step reads one contiguous 16 KiB block per
+// full-width slice and a table fill is a plain copy of contiguous rows.
+template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB, bool BUF, bool PREP>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
   constexpr int kMaxRB = NRB;
@@ -196,6 +184,18 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   for (int cb = 0; cb < kCB; ++cb)
     tcol[cb] = (MODE == kSwiGLU ? (cb < kHalf ? 8 * kCB * wave + 16 * cb : kCols / 2 + 8 * kCB * wave + 16 * (cb - kHalf))
                                 : 16 * kCB * wave + 16 * cb) + c16;
+  // PREP: the item lies in full-width slice pslice (a half-width item is
+  // half `phalf` of one); the table holds that slice's 256 columns, and lcol
+  // is the table column of each column block (lane column 0)
+  const int pslice = kCols == kColsMax ? U.slice : (U.slice >> 1);
+  const int phalf = kCols == kColsMax ? 0 : (U.slice & 1);
+  int lcol[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    lcol[cb] = MODE == kSwiGLU ? (cb < kHalf ? 0 : kColsMax / 2) + phalf * (kCols / 2) + wave * 8 * kCB + 16 * (cb % kHalf)
+                               : phalf * kCols + wave * 16 * kCB + 16 * cb;
+    if (PREP) tcol[cb] = lcol[cb] + c16;
+  }
   auto tab_row = [&](int c) -> int {
     if (MODE == kSwiGLU) {
       const int f = N >> 1, n = U.slice * (kCols / 2) + (c & (kCols / 2 - 1));
@@ -221,15 +221,21 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // BUF (K a multiple of the step, so no lane ever reads past K): codes by
   // buffer loads at lane offset 4 b_row + 16 kq bytes and step offset 64 s
   // bytes.
-  const __amdgpu_buffer_rsrc_t rsrc_b = raw_rsrc(wq);
+  // PREP: the lane's 16 bytes of chunk prep_chunk(lcol) of the slice's block
+  // for step s, at step offset 16 KiB s.
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      raw_rsrc(PREP ? (const void *)(P.Pq + (int64_t)U.e * P.pq_estride) : (const void *)wq);
   uint32_t b_voff[kCB];
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) b_voff[cb] = 4u * b_row[cb] + 16u * (uint32_t)kq;
+  for (int cb = 0; cb < kCB; ++cb)
+    b_voff[cb] = PREP ? (uint32_t)pslice * (uint32_t)steps * (uint32_t)kPrepBlock +
+                            1024u * (uint32_t)prep_chunk(lcol[cb], MODE == kSwiGLU) + 16u * (uint32_t)lane
+                      : 4u * b_row[cb] + 16u * (uint32_t)kq;
   auto load_b = [&](Stage &st, int s) {
     if constexpr (BUF) {
+      const uint32_t so = PREP ? (uint32_t)kPrepBlock * (uint32_t)s : 64u * (uint32_t)s;
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-        st.q[cb] = __builtin_bit_cast(u4, buf_load16(rsrc_b, b_voff[cb], 64u * (uint32_t)s));
+      for (int cb = 0; cb < kCB; ++cb) st.q[cb] = __builtin_bit_cast(u4, buf_load16(rsrc_b, b_voff[cb], so));
       return;
     }
     const int k0 = lane_k0(s);
@@ -256,6 +262,28 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // per step and lane.
   auto fill_table = [&](int gc) {
     const int g0 = kTabGroups * gc, GC = min(kTabGroups, G - g0);
+    if constexpr (PREP) {
+      // rows g0 .. g0 + GC - 1 of the slice's prepared table, 16 bytes per
+      // thread and pass, every load issued before the first store
+      static_assert(kTabGroups * kColsMax / 4 % kGemmThreads == 0, "whole passes of the table copy");
+      constexpr int kIt = kTabGroups * kColsMax / 4 / kGemmThreads;
+      const __amdgpu_buffer_rsrc_t rt = raw_rsrc(P.Pt + (int64_t)U.e * P.pt_estride);
+      const uint32_t base = 4u * (uint32_t)((pslice * G + g0) * kColsMax);  // bytes
+      const int n16 = GC * (kColsMax / 4);
+      uint4 v[kIt];
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int i = min(tid + it * kGemmThreads, n16 - 1);
+        v[it] = buf_load16(rt, base + 16u * (uint32_t)i, 0u);
+      }
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int i = tid + it * kGemmThreads;
+        if (i < n16)
+          *reinterpret_cast<uint4 *>(&tab[(i / (kColsMax / 4)) * kTabStride + 4 * (i % (kColsMax / 4))]) = v[it];
+      }
+      return;
+    }
     if ((G & 7) == 0 && (GC & 7) == 0) {
       // every load is issued before the first conversion, so the fill costs
       // one memory round trip
@@ -283,8 +311,8 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
           const uint32_t bw[4] = {bv[it].x, bv[it].y, bv[it].z, bv[it].w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            tab[(8 * q8 + 2 * u) * kTabStride + c] = live ? pack_scale_bias(sw[u] & 0xFFFFu, bw[u] & 0xFFFFu) : 0u;
-            tab[(8 * q8 + 2 * u + 1) * kTabStride + c] = live ? pack_scale_bias(sw[u] >> 16, bw[u] >> 16) : 0u;
+            tab[(8 * q8 + 2 * u) * kTabStride + c] = live ? rb_pack_scale_bias(sw[u] & 0xFFFFu, bw[u] & 0xFFFFu) : 0u;
+            tab[(8 * q8 + 2 * u + 1) * kTabStride + c] = live ? rb_pack_scale_bias(sw[u] >> 16, bw[u] >> 16) : 0u;
           }
         }
       }
@@ -293,7 +321,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
         const int c = i / GC, gg = i - c * GC;
         const int n = tab_row(c);
         tab[gg * kTabStride + c] =
-            n >= 0 ? pack_scale_bias(wsc[(int64_t)n * G + g0 + gg], wbi[(int64_t)n * G + g0 + gg]) : 0u;
+            n >= 0 ? rb_pack_scale_bias(wsc[(int64_t)n * G + g0 + gg], wbi[(int64_t)n * G + g0 + gg]) : 0u;
       }
     }
   };
@@ -371,44 +399,25 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t m_lo = vgpr_const(0x000F000Fu), m_hi = vgpr_const(0x00F000F0u);
-  const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
+  const RbConsts rbk = rb_consts();
 
   auto compute = [&](const Stage &st, int s, int buf) {
     const int k0 = lane_k0(s);
     const bool kvalid = k0 < K;
     const int gt = ((k0 >> 6) & (kTabGroups - 1)) * kTabStride;  // group row in the table
-    h2 s1[kCB], s16[kCB], cc[kCB];
+    RbGroup grp[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB && !WX; ++cb) {
       const uint32_t tv = kvalid ? tab[gt + tcol[cb]] : 0u;
-      const h2 sc = __builtin_bit_cast(h2, tv);
-      s1[cb] = h2{sc[0], sc[0]};
-      s16[cb] = s1[cb] * h2{(_Float16)0.0625f, (_Float16)0.0625f};
-      cc[cb] = h2{sc[1], sc[1]};
+      grp[cb] = rb_group(tv);
     }
-    const h2 off1 = h2{(_Float16)-1032.f, (_Float16)-1032.f};
-    const h2 off16 = h2{(_Float16)-1152.f, (_Float16)-1152.f};
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
     // rebuild the 32 codes of quarter-step j for column block cb
     auto rebuild = [&](int j, int cb) -> h8 {
       // expanded weights: inputs past K (the last step's loads were clamped
       // to the row start) contribute zero, as the zero table does below
       if constexpr (WX) return kvalid ? __builtin_bit_cast(h8, st.q[cb][j]) : h8{};
-      else {
-      const uint32_t w = st.q[cb][j];
-      const uint32_t w8 = w >> 8;
-      // (q0,q4) (16q1,16q5) (q2,q6) (16q3,16q7) as fp16 1024+v, exact
-      const h2 t0 = __builtin_bit_cast(h2, (w & m_lo) | magic) + off1;
-      const h2 t1 = __builtin_bit_cast(h2, (w & m_hi) | magic) + off16;
-      const h2 t2 = __builtin_bit_cast(h2, (w8 & m_lo) | magic) + off1;
-      const h2 t3 = __builtin_bit_cast(h2, (w8 & m_hi) | magic) + off16;
-      const h2 w0 = __builtin_elementwise_fma(t0, s1[cb], cc[cb]);
-      const h2 w1 = __builtin_elementwise_fma(t1, s16[cb], cc[cb]);
-      const h2 w2 = __builtin_elementwise_fma(t2, s1[cb], cc[cb]);
-      const h2 w3 = __builtin_elementwise_fma(t3, s16[cb], cc[cb]);
-      return h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
-      }
+      else return rb_rebuild_g(st.q[cb][j], grp[cb], rbk);
     };
     auto read_a = [&](int j, int rb) -> h8 {
       const int aoff = 16 * ((4 * kq + j) ^ c16);
@@ -588,16 +597,16 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 }
 
 // The unit's 16-row block count picks the compiled form.
-template <int MODE, bool AF16, bool WX, bool CHECK, int CB, bool BUF>
+template <int MODE, bool AF16, bool WX, bool CHECK, int CB, bool BUF, bool PREP>
 __device__ __forceinline__ void run_rows(const GemmProblem &P, const Unit &U, uint8_t *lds, const int *s_arow,
                                          uint32_t *tab) {
   switch ((U.nr + 15) >> 4) {
-    case 1: run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF>(P, U, lds, s_arow, tab); break;
-    case 2: run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF>(P, U, lds, s_arow, tab); break;
-    case 3: run_unit<MODE, AF16, WX, CHECK, 3, CB, BUF>(P, U, lds, s_arow, tab); break;
-    case 4: run_unit<MODE, AF16, WX, CHECK, 4, CB, BUF>(P, U, lds, s_arow, tab); break;
-    case 5: run_unit<MODE, AF16, WX, CHECK, 5, CB, BUF>(P, U, lds, s_arow, tab); break;
-    default: run_unit<MODE, AF16, WX, CHECK, 6, CB, BUF>(P, U, lds, s_arow, tab); break;
+    case 1: run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    case 2: run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    case 3: run_unit<MODE, AF16, WX, CHECK, 3, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    case 4: run_unit<MODE, AF16, WX, CHECK, 4, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    case 5: run_unit<MODE, AF16, WX, CHECK, 5, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    default: run_unit<MODE, AF16, WX, CHECK, 6, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
   }
 }
 
@@ -658,14 +667,20 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
 
   // half-width items: the same code with half the column blocks per wave
   // (always, for expanded weights: their stages take four times the registers)
+  // prepared weights (the host sets Pq only when K is a multiple of the
+  // step), else buffer loads when K is a multiple of the step
   constexpr bool kCanBuf = AF16 && !WX;
+  constexpr bool kCanPrep = kCanBuf && MODE != kStoreC;  // the layer's projections
   const bool buf = kCanBuf && (P.K & (kKStep - 1)) == 0;
+  const bool prep = buf && MODE != kStoreC && P.Pq != nullptr;
   if (WX || narrow) {
-    if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf>(P, U, lds, s_arow, tab);
-    else     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, false>(P, U, lds, s_arow, tab);
+    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
+    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, false>(P, U, lds, s_arow, tab);
+    else          run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, false, false>(P, U, lds, s_arow, tab);
   } else {
-    if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf>(P, U, lds, s_arow, tab);
-    else     run_rows<MODE, AF16, WX, CHECK, kCBFull, false>(P, U, lds, s_arow, tab);
+    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
+    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, false>(P, U, lds, s_arow, tab);
+    else          run_rows<MODE, AF16, WX, CHECK, kCBFull, false, false>(P, U, lds, s_arow, tab);
   }
 }
 
@@ -722,6 +737,58 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint32_t *q, const ui
   const uint32_t packed = rb_pack_scale_bias(sc[gi], bi[gi]);
   const rb_h8 w = rb_rebuild(q[i], packed, rb_consts());
   reinterpret_cast<rb_h8 *>(out)[i] = w;
+}
+
+// Prepared codes (prep_layout.h): one thread per 16-byte chunk, i.e. per
+// (expert, slice, step, wave, block, lane).
+__global__ __launch_bounds__(256) void prep_codes_kernel(const uint32_t *q, int E, int N, int K, bool swiglu,
+                                                         uint4 *pq) {
+  const int steps = K / kPrepStep;
+  const int64_t per_e = (int64_t)prep_slices(N, swiglu) * steps * (kPrepBlock / 16);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_e * E) return;
+  const int e = (int)(i / per_e);
+  const int64_t r = i - e * per_e;
+  const int blk = (int)(r >> 10), in = (int)(r & 1023);
+  const int t = blk / steps, st = blk - t * steps;
+  const int chunk = in >> 6, lane = in & 63;
+  const int w = chunk >> 2, b = chunk & 3, qq = lane >> 4, c = lane & 15;
+  const int lc = (swiglu ? (b < 2 ? 32 * w + 16 * b : 128 + 32 * w + 16 * (b - 2)) : 64 * w + 16 * b) + c;
+  const int n = prep_row(t, lc, N, swiglu);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (n >= 0)
+    v = *reinterpret_cast<const uint4 *>(q + (int64_t)e * N * (K / 8) + (int64_t)n * (K / 8) + 16 * st + 4 * qq);
+  pq[i] = v;
+}
+
+// Prepared table: one thread per (expert, slice, group, table column) dword.
+__global__ __launch_bounds__(256) void prep_table_kernel(const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
+                                                         bool swiglu, uint32_t *pt) {
+  const int G = K / 64;
+  const int64_t per_e = (int64_t)prep_slices(N, swiglu) * G * kPrepCols;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_e * E) return;
+  const int e = (int)(i / per_e);
+  const int64_t r = i - e * per_e;
+  const int c = (int)(r % kPrepCols), tg = (int)(r / kPrepCols);
+  const int t = tg / G, g = tg - t * G;
+  const int n = prep_row(t, c, N, swiglu);
+  const int64_t gi = (int64_t)e * N * G + (int64_t)n * G + g;
+  pt[i] = n >= 0 ? rb_pack_scale_bias(sc[gi], bi[gi]) : 0u;
+}
+
+hipError_t launch_prepare(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
+                          bool swiglu, uint8_t *pq, uint32_t *pt, hipStream_t s) {
+  const int64_t n16 = (int64_t)E * prep_code_bytes(N, K, swiglu) / 16;
+  const int64_t nt = (int64_t)E * prep_table_dwords(N, K, swiglu);
+  if (n16 > 0)
+    hipLaunchKernelGGL(prep_codes_kernel, dim3((unsigned)ceil_div(n16, 256)), dim3(256), 0, s, q, E, N, K, swiglu,
+                       reinterpret_cast<uint4 *>(pq));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nt == 0) return err;
+  hipLaunchKernelGGL(prep_table_kernel, dim3((unsigned)ceil_div(nt, 256)), dim3(256), 0, s, sc, bi, E, N, K, swiglu,
+                     pt);
+  return hipGetLastError();
 }
 
 hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int64_t rows, int K,

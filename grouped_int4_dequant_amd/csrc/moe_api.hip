@@ -9,6 +9,7 @@
 //            Qwen3.6-35B-A3B en Apple Silicon" (7minutos.es)
 
 #include "moe_internal.h"
+#include "prep_layout.h"
 
 #include <algorithm>
 #include <mutex>
@@ -99,7 +100,53 @@ int check_layer(const moe_layer_t *L) {
     for (const void *p : sh)
       if (!p || !aligned16(p)) return MOE_EINVAL;
   }
+  if (L->prep && ((uintptr_t)L->prep % kAlign)) return MOE_EINVAL;
   return MOE_OK;
+}
+
+// Where each projection's prepared codes and table sit in a prepared copy
+// (byte offsets from its start; prep_layout.h gives the order inside).
+struct PrepLayout {
+  int64_t gu_q, gu_t, dn_q, dn_t, sh_gu_q, sh_gu_t, sh_dn_q, sh_dn_t, total;
+};
+
+bool prep_supported(const moe_layer_t *L) { return L->d % 128 == 0 && L->f % 128 == 0 && L->f_sh % 128 == 0; }
+
+PrepLayout prep_layout(const moe_layer_t *L) {
+  const int d = L->d, f = L->f, fs = L->f_sh;
+  const int64_t E = L->E;
+  PrepLayout p{};
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = at;
+    at += round_up(bytes, kAlign);
+    return o;
+  };
+  p.gu_q = take(E * prep_code_bytes(2 * f, d, true));
+  p.gu_t = take(E * prep_table_dwords(2 * f, d, true) * 4);
+  p.dn_q = take(E * prep_code_bytes(d, f, false));
+  p.dn_t = take(E * prep_table_dwords(d, f, false) * 4);
+  p.sh_gu_q = p.sh_gu_t = p.sh_dn_q = p.sh_dn_t = -1;
+  if (fs > 0) {
+    p.sh_gu_q = take(prep_code_bytes(2 * fs, d, true));
+    p.sh_gu_t = take(prep_table_dwords(2 * fs, d, true) * 4);
+    p.sh_dn_q = take(prep_code_bytes(d, fs, false));
+    p.sh_dn_t = take(prep_table_dwords(d, fs, false) * 4);
+  }
+  p.total = at;
+  return p;
+}
+
+// Point a GEMM problem at the prepared copy of one projection (expert
+// stride from the layout), when the layer has one.
+void use_prep(GemmProblem &p, const moe_layer_t *L, int64_t q_ofs, int64_t t_ofs, int N, int K, bool swiglu,
+              bool per_expert) {
+  if (!L->prep || !prep_supported(L)) return;
+  const uint8_t *base = static_cast<const uint8_t *>(L->prep);
+  p.Pq = base + q_ofs;
+  p.Pt = reinterpret_cast<const uint32_t *>(base + t_ofs);
+  p.pq_estride = per_expert ? prep_code_bytes(N, K, swiglu) : 0;
+  p.pt_estride = per_expert ? prep_table_dwords(N, K, swiglu) : 0;
 }
 
 int check_routing(const moe_routing_t *r) {
@@ -377,6 +424,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
   }
 
   // concurrent form: the shared expert on the side stream, beside the routing
+  const PrepLayout pl = prep_layout(L);
   const bool split = opt.side != nullptr && fs > 0 && !opt.unfused;
   if (split) {
     if (hipEventRecord(opt.fork, s) != hipSuccess || hipStreamWaitEvent(opt.side, opt.fork, 0) != hipSuccess)
@@ -398,6 +446,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     GemmProblem &q = gd.prob[0];
     q.A = w.h_sh; q.lda = fs; q.a_row = nullptr;
     q.Wq = L->sh_dn_q; q.Ws = L->sh_dn_s; q.Wb = L->sh_dn_b;
+    use_prep(q, L, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
     q.N = d; q.K = fs;
     q.units = nullptr; q.num_units = nullptr; q.implicit_rows = T; q.unit_rows = opt.shared_unit_rows;
     q.nslices = (int)ceil_div(d, kGemmCols);
@@ -443,6 +492,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = 2 * fs; p.K = d;
     p.Wx = wx ? wx + (int64_t)E * 2 * f * d : nullptr; p.wx_estride = 0;
+    if (!opt.unfused) use_prep(p, L, pl.sh_gu_q, pl.sh_gu_t, 2 * fs, d, true, false);
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(fs, hcols);
     p.wg_begin = nwg;
@@ -457,6 +507,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)2 * f * (d / 8); p.ws_estride = (int64_t)2 * f * (d / 64);
     p.N = 2 * f; p.K = d;
     p.Wx = wx; p.wx_estride = (int64_t)2 * f * d;
+    if (!opt.unfused) use_prep(p, L, pl.gu_q, pl.gu_t, 2 * f, d, true, true);
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(f, hcols);
     p.ntail = opt.ntail;
@@ -489,6 +540,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = d; p.K = fs;
     p.Wx = wx ? wx + (int64_t)E * d * f : nullptr; p.wx_estride = 0;
+    if (!opt.unfused) use_prep(p, L, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(d, ocols);
     p.wg_begin = nwg;
@@ -503,6 +555,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)d * (f / 8); p.ws_estride = (int64_t)d * (f / 64);
     p.N = d; p.K = f;
     p.Wx = wx; p.wx_estride = (int64_t)d * f;
+    if (!opt.unfused) use_prep(p, L, pl.dn_q, pl.dn_t, d, f, false, true);
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(d, ocols);
     p.ntail = opt.ntail > 0 ? kNarrowTailDown : 0;  // ablation forms: no tail
@@ -534,6 +587,34 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
   if (T < 0 || E <= 0 || E > MOE_MAX_EXPERTS || T > kMaxRouteTokens) return 0;
   // per-sub-chunk expert counts
   return (size_t)round_up(std::max<int64_t>(ceil_div(T, kSubChunk), 1) * E * (int64_t)sizeof(int32_t), kAlign);
+}
+
+size_t moe_prepared_bytes(const moe_layer_t *L) {
+  if (!L || L->d <= 0 || L->f <= 0 || L->E <= 0 || L->f_sh < 0 || L->E > MOE_MAX_EXPERTS) return 0;
+  if (!prep_supported(L)) return 0;
+  return (size_t)prep_layout(L).total;
+}
+
+int moe_prepare_weights(const moe_layer_t *L, void *dst, size_t dst_bytes, hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (!dst || ((uintptr_t)dst % kAlign)) return MOE_EINVAL;
+  if (!prep_supported(L)) return MOE_EUNSUPPORTED;
+  const PrepLayout pl = prep_layout(L);
+  if (dst_bytes < (size_t)pl.total) return MOE_EWORKSPACE;
+  uint8_t *b = static_cast<uint8_t *>(dst);
+  const int d = L->d, f = L->f, fs = L->f_sh, E = L->E;
+  auto tab = [&](int64_t o) { return reinterpret_cast<uint32_t *>(b + o); };
+  st = hip_status(launch_prepare(L->gu_q, L->gu_s, L->gu_b, E, 2 * f, d, true, b + pl.gu_q, tab(pl.gu_t), stream));
+  if (st == MOE_OK)
+    st = hip_status(launch_prepare(L->dn_q, L->dn_s, L->dn_b, E, d, f, false, b + pl.dn_q, tab(pl.dn_t), stream));
+  if (st == MOE_OK && fs > 0)
+    st = hip_status(launch_prepare(L->sh_gu_q, L->sh_gu_s, L->sh_gu_b, 1, 2 * fs, d, true, b + pl.sh_gu_q,
+                                   tab(pl.sh_gu_t), stream));
+  if (st == MOE_OK && fs > 0)
+    st = hip_status(launch_prepare(L->sh_dn_q, L->sh_dn_s, L->sh_dn_b, 1, d, fs, false, b + pl.sh_dn_q,
+                                   tab(pl.sh_dn_t), stream));
+  return st;
 }
 
 size_t moe_workspace_bytes(int32_t T, const moe_layer_t *L) {

@@ -127,6 +127,11 @@ struct GemmProblem {
   int nslices;               // workgroups per unit along N
   int ntail;                 // listed units: about this many trailing units run as 2*nslices half-width items
   int wg_begin;              // first workgroup (in remapped order) of this problem
+  // prepared weights (nullptr: read Wq/Ws/Wb): codes in tile order and the
+  // (fp16 s, fp16 b + 8 s) table in table order, per expert (K a multiple of
+  // 128; layout in prep_layout.h)
+  const uint8_t *Pq; int64_t pq_estride;   // bytes
+  const uint32_t *Pt; int64_t pt_estride;  // dwords
   // outputs
   float *C; int ldc;          // kStoreC
   uint16_t *H; int ldh;       // kSwiGLU (permuted-run columns), kStoreH (natural columns)
@@ -145,6 +150,10 @@ struct GemmArgs {
 // kSwiGLU and kStoreH).
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr, bool expanded = false);
+// Prepared copy of one projection's weights for E experts (prep_layout.h):
+// swiglu: rows 0..N/2-1 gate, N/2..N-1 up.
+hipError_t launch_prepare(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
+                          bool swiglu, uint8_t *pq, uint32_t *pt, hipStream_t s);
 // Unfused ablation: weights of rows x K expanded into fp16 (rebuild order).
 hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int64_t rows, int K,
                          uint16_t *out, hipStream_t s);

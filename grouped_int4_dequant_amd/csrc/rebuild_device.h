@@ -50,13 +50,25 @@ __device__ __forceinline__ RbConsts rb_consts() {
   return RbConsts{rb_vgpr_const(0x000F000Fu), rb_vgpr_const(0x00F000F0u)};
 }
 
-// Eight weights of one code word; sc = packed (fp16 s, fp16 (b + 8 s)).
-__device__ __forceinline__ rb_h8 rb_rebuild(uint32_t w, uint32_t sc_packed, const RbConsts &k) {
-  const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
+// A group's constants as the rebuild applies them: (s, s), (s/16, s/16) and
+// (b + 8 s, b + 8 s) from the packed pair. For a bf16 scale (8 significant
+// bits) s/16 is exact in fp16 from s = 2^-13 up; below that it is a
+// subnormal without room for every bit.
+struct RbGroup {
+  rb_h2 s1, s16, cc;
+};
+__device__ __forceinline__ RbGroup rb_group(uint32_t sc_packed) {
   const rb_h2 sc = __builtin_bit_cast(rb_h2, sc_packed);
-  const rb_h2 s1 = rb_h2{sc[0], sc[0]};
-  const rb_h2 s16 = s1 * rb_h2{(_Float16)0.0625f, (_Float16)0.0625f};
-  const rb_h2 cc = rb_h2{sc[1], sc[1]};
+  RbGroup g;
+  g.s1 = rb_h2{sc[0], sc[0]};
+  g.s16 = g.s1 * rb_h2{(_Float16)0.0625f, (_Float16)0.0625f};
+  g.cc = rb_h2{sc[1], sc[1]};
+  return g;
+}
+
+// Eight weights of one code word with its group's constants.
+__device__ __forceinline__ rb_h8 rb_rebuild_g(uint32_t w, const RbGroup &g, const RbConsts &k) {
+  const uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024)
   const rb_h2 off1 = rb_h2{(_Float16)-1032.f, (_Float16)-1032.f};
   const rb_h2 off16 = rb_h2{(_Float16)-1152.f, (_Float16)-1152.f};
   const uint32_t w8 = w >> 8;
@@ -64,11 +76,16 @@ __device__ __forceinline__ rb_h8 rb_rebuild(uint32_t w, uint32_t sc_packed, cons
   const rb_h2 t1 = __builtin_bit_cast(rb_h2, (w & k.m_hi) | magic) + off16;   // 16 (q1, q5)
   const rb_h2 t2 = __builtin_bit_cast(rb_h2, (w8 & k.m_lo) | magic) + off1;   // (q2, q6)
   const rb_h2 t3 = __builtin_bit_cast(rb_h2, (w8 & k.m_hi) | magic) + off16;  // 16 (q3, q7)
-  const rb_h2 w0 = __builtin_elementwise_fma(t0, s1, cc);
-  const rb_h2 w1 = __builtin_elementwise_fma(t1, s16, cc);
-  const rb_h2 w2 = __builtin_elementwise_fma(t2, s1, cc);
-  const rb_h2 w3 = __builtin_elementwise_fma(t3, s16, cc);
+  const rb_h2 w0 = __builtin_elementwise_fma(t0, g.s1, g.cc);
+  const rb_h2 w1 = __builtin_elementwise_fma(t1, g.s16, g.cc);
+  const rb_h2 w2 = __builtin_elementwise_fma(t2, g.s1, g.cc);
+  const rb_h2 w3 = __builtin_elementwise_fma(t3, g.s16, g.cc);
   return rb_h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+}
+
+// Eight weights of one code word; sc = packed (fp16 s, fp16 (b + 8 s)).
+__device__ __forceinline__ rb_h8 rb_rebuild(uint32_t w, uint32_t sc_packed, const RbConsts &k) {
+  return rb_rebuild_g(w, rb_group(sc_packed), k);
 }
 
 // Eight consecutive activations (natural order) -> fp16 in the rebuild order

@@ -83,6 +83,12 @@ extern "C" {
  *   sh_*  the same for the shared expert without the E dimension and with
  *         f_sh in place of f; f_sh == 0 means the layer has no shared expert
  *         and the sh_* pointers are ignored.
+ *   prep  NULL, or a prepared copy of the same weights written by
+ *         moe_prepare_weights for this layer (256-byte aligned, kept alive
+ *         and unchanged by the caller). When set, the prefill grouped GEMMs
+ *         read it instead of the arrays above (same arithmetic, results equal
+ *         bit for bit); the few-token form and the ablation forms still read
+ *         the arrays, which must stay valid.
  * All weight pointers must be 16-byte aligned.
  */
 typedef struct moe_layer {
@@ -91,7 +97,36 @@ typedef struct moe_layer {
   const uint32_t *dn_q;    const uint16_t *dn_s,    *dn_b;
   const uint32_t *sh_gu_q; const uint16_t *sh_gu_s, *sh_gu_b;
   const uint32_t *sh_dn_q; const uint16_t *sh_dn_s, *sh_dn_b;
+  const void *prep;
 } moe_layer_t;
+
+/*
+ * Bytes of device memory a prepared copy of L's weights takes (about the
+ * size of the weights themselves: the same codes, and one 4-byte pair per
+ * group in place of the bf16 scale and bias), or 0 when L is invalid or d,
+ * f or f_sh is not a multiple of 128. Host-only: reads L's scalar fields.
+ */
+size_t moe_prepared_bytes(const moe_layer_t *L);
+
+/*
+ * Write the prepared copy of L's weights into dst (device memory of at least
+ * moe_prepared_bytes(L) bytes, 256-byte aligned), enqueued on stream; then
+ * set L->prep = dst (the caller does) to have the prefill GEMMs use it.
+ * The copy holds the same 4-bit codes rearranged so that one workgroup item
+ * of the grouped GEMM reads each 128-input step of its 256 output columns as
+ * one contiguous 16 KiB block, and each group's (fp16 s, fp16 (b + 8 s))
+ * pair, the constants of the on-chip rebuild, already formed and in the
+ * order of the item's LDS table (Lily-EN "Prefill: Keep Weights Packed,
+ * Keep Routing on the GPU": the weights stay 4-bit in memory; the layout is
+ * this library's). dst then holds, each part starting at a multiple of 256
+ * bytes: the routed experts' gate/up codes, their table, the routed down
+ * codes, their table, and (f_sh > 0) the same four parts of the shared
+ * expert. One-time work per layer (a few hundred microseconds per GB).
+ * L->prep is ignored. Errors: MOE_EINVAL (invalid layer, null or
+ * misaligned dst), MOE_EUNSUPPORTED (d, f or f_sh not a multiple of 128),
+ * MOE_EWORKSPACE (dst_bytes too small), MOE_EHIP.
+ */
+int moe_prepare_weights(const moe_layer_t *L, void *dst, size_t dst_bytes, hipStream_t stream);
 
 /*
  * Routing outputs for T tokens (Lily-EN "Prefill: Keep Weights Packed, Keep

@@ -55,6 +55,35 @@ def test_workspace_sizes():
     assert lib.moe_route_workspace_bytes(2048, 4096) == 0
 
 
+def test_prepared_bytes():
+    lib = moe.load()
+    L = qwen_layer_struct()
+    MiB = 2 ** 20
+    # the same bytes as the weights: codes (1 + 0.5 MiB per expert), one
+    # 4-byte pair per group (128 + 64 KiB per expert), and the shared expert's
+    expect = 256 * (MiB + MiB // 2) + 256 * (128 + 64) * 1024 + (MiB + MiB // 2 + 192 * 1024)
+    assert lib.moe_prepared_bytes(ctypes.byref(L)) == expect
+    assert lib.moe_prepared_bytes(ctypes.byref(qwen_layer_struct(f_sh=0))) == expect - (MiB + MiB // 2 + 192 * 1024)
+    # d, f or f_sh not a multiple of 128: no prepared form
+    for kw in (dict(d=320), dict(f=192), dict(f_sh=64)):
+        assert lib.moe_prepared_bytes(ctypes.byref(qwen_layer_struct(**kw))) == 0
+    assert lib.moe_prepared_bytes(None) == 0
+
+
+def test_prepare_weights_rejects():
+    lib = moe.load()
+    L = qwen_layer_struct()
+    n = lib.moe_prepared_bytes(ctypes.byref(L))
+    assert lib.moe_prepare_weights(ctypes.byref(L), 0x1010, n, None) == B.MOE_EINVAL       # misaligned
+    assert lib.moe_prepare_weights(ctypes.byref(L), None, n, None) == B.MOE_EINVAL
+    assert lib.moe_prepare_weights(ctypes.byref(L), 0x1000, n - 1, None) == B.MOE_EWORKSPACE
+    bad = qwen_layer_struct(d=320)
+    assert lib.moe_prepare_weights(ctypes.byref(bad), 0x1000, n, None) == B.MOE_EUNSUPPORTED
+    # a layer whose prepared copy is misaligned is rejected by the forward call
+    L.prep = 0x1010
+    assert lib.moe_layer_forward(ctypes.byref(L), 0x1000, 0x1000, 16, 0x1000, None, 0x1000, 1 << 30, None) == B.MOE_EINVAL
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
