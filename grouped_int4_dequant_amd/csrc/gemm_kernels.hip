@@ -20,7 +20,10 @@
 //     items with two blocks per wave, so the final round of workgroups is
 //     made of half-length pieces.
 //   * Each group's scale and bias are read once per work unit with coalesced
-//     loads into an LDS table of fp16 (s, b + 8s) pairs.
+//     loads into an LDS table of fp16 (s, b + 8s) pairs; with a prepared copy
+//     of the weights (prep_layout.h: codes in the order the item reads them,
+//     the pairs pre-formed) each lane instead loads its pairs beside its
+//     codes, and every K step of an item reads one contiguous 16 KiB block.
 //   * Weights go HBM -> VGPR with one 128-bit load per lane and column block
 //     per K step, one step ahead of use (buffer loads whose per-step offset
 //     sits in a scalar register when K is a multiple of the step, so stepping
@@ -86,7 +89,9 @@ static_assert(MOE_GEMM_WGS_PER_CU * (2 * kBufBytes + kTabGroups * kTabStride * 4
 template <int CB>
 struct BStage {
   u4 q[CB];            // 4 code words (32 codes) per column block
+  uint32_t t[CB];      // prepared weights: the block's (s, b + 8 s) pair for this step
 };
+
 
 // Weights already expanded to fp16 in device memory (the unfused ablation):
 // the lane's 32 weights of each column block as four 8-weight chunks.
@@ -136,9 +141,10 @@ struct Unit {
 // the K loop's loads are buffer loads with the step offset in a scalar
 // register; otherwise per-lane clamped addresses keep the last step's
 // quarters past K on their row.
-// PREP (implies BUF): codes and the scale/bias table come from the prepared
-// copy (prep_layout.h): every K step reads one contiguous 16 KiB block per
-// full-width slice and a table fill is a plain copy of contiguous rows.
+// PREP (implies BUF): codes and the scale/bias pairs come from the prepared
+// copy (prep_layout.h): every K step reads one contiguous 16 KiB block of
+// codes per full-width slice, and each lane loads its column blocks' pairs
+// for the step beside them, so the LDS table is not used.
 template <int MODE, bool AF16, bool WX, bool CHECK, int NRB, int CB, bool BUF, bool PREP>
 __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, uint8_t *lds,
                                          const int *s_arow, uint32_t *tab) {
@@ -185,8 +191,8 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     tcol[cb] = (MODE == kSwiGLU ? (cb < kHalf ? 8 * kCB * wave + 16 * cb : kCols / 2 + 8 * kCB * wave + 16 * (cb - kHalf))
                                 : 16 * kCB * wave + 16 * cb) + c16;
   // PREP: the item lies in full-width slice pslice (a half-width item is
-  // half `phalf` of one); the table holds that slice's 256 columns, and lcol
-  // is the table column of each column block (lane column 0)
+  // half `phalf` of one); lcol is the prepared table column of each column
+  // block (lane column 0)
   const int pslice = kCols == kColsMax ? U.slice : (U.slice >> 1);
   const int phalf = kCols == kColsMax ? 0 : (U.slice & 1);
   int lcol[kCB];
@@ -194,7 +200,6 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   for (int cb = 0; cb < kCB; ++cb) {
     lcol[cb] = MODE == kSwiGLU ? (cb < kHalf ? 0 : kColsMax / 2) + phalf * (kCols / 2) + wave * 8 * kCB + 16 * (cb % kHalf)
                                : phalf * kCols + wave * 16 * kCB + 16 * cb;
-    if (PREP) tcol[cb] = lcol[cb] + c16;
   }
   auto tab_row = [&](int c) -> int {
     if (MODE == kSwiGLU) {
@@ -231,11 +236,25 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     b_voff[cb] = PREP ? (uint32_t)pslice * (uint32_t)steps * (uint32_t)kPrepBlock +
                             1024u * (uint32_t)prep_chunk(lcol[cb], MODE == kSwiGLU) + 16u * (uint32_t)lane
                       : 4u * b_row[cb] + 16u * (uint32_t)kq;
+  // PREP: each lane loads its column blocks' (s, b + 8 s) pairs for the step
+  // straight from the prepared table with the codes, group 2 s + kq / 2 of
+  // the slice (step offset 2 KiB s): no LDS table, no fills, no refill
+  // barriers
+  const __amdgpu_buffer_rsrc_t rsrc_t = raw_rsrc(P.Pt + (int64_t)U.e * P.pt_estride);
+  uint32_t t_voff[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+    t_voff[cb] = 4u * (uint32_t)((pslice * G + (kq >> 1)) * kColsMax + lcol[cb] + c16);
   auto load_b = [&](Stage &st, int s) {
     if constexpr (BUF) {
       const uint32_t so = PREP ? (uint32_t)kPrepBlock * (uint32_t)s : 64u * (uint32_t)s;
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) st.q[cb] = __builtin_bit_cast(u4, buf_load16(rsrc_b, b_voff[cb], so));
+      if constexpr (PREP) {
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          st.t[cb] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_t, t_voff[cb], 2048u * (uint32_t)s, 0);
+      }
       return;
     }
     const int k0 = lane_k0(s);
@@ -262,28 +281,6 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // per step and lane.
   auto fill_table = [&](int gc) {
     const int g0 = kTabGroups * gc, GC = min(kTabGroups, G - g0);
-    if constexpr (PREP) {
-      // rows g0 .. g0 + GC - 1 of the slice's prepared table, 16 bytes per
-      // thread and pass, every load issued before the first store
-      static_assert(kTabGroups * kColsMax / 4 % kGemmThreads == 0, "whole passes of the table copy");
-      constexpr int kIt = kTabGroups * kColsMax / 4 / kGemmThreads;
-      const __amdgpu_buffer_rsrc_t rt = raw_rsrc(P.Pt + (int64_t)U.e * P.pt_estride);
-      const uint32_t base = 4u * (uint32_t)((pslice * G + g0) * kColsMax);  // bytes
-      const int n16 = GC * (kColsMax / 4);
-      uint4 v[kIt];
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int i = min(tid + it * kGemmThreads, n16 - 1);
-        v[it] = buf_load16(rt, base + 16u * (uint32_t)i, 0u);
-      }
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int i = tid + it * kGemmThreads;
-        if (i < n16)
-          *reinterpret_cast<uint4 *>(&tab[(i / (kColsMax / 4)) * kTabStride + 4 * (i % (kColsMax / 4))]) = v[it];
-      }
-      return;
-    }
     if ((G & 7) == 0 && (GC & 7) == 0) {
       // every load is issued before the first conversion, so the fill costs
       // one memory round trip
@@ -408,7 +405,9 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
     RbGroup grp[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB && !WX; ++cb) {
-      const uint32_t tv = kvalid ? tab[gt + tcol[cb]] : 0u;
+      uint32_t tv;
+      if constexpr (PREP) tv = st.t[cb];
+      else tv = kvalid ? tab[gt + tcol[cb]] : 0u;
       grp[cb] = rb_group(tv);
     }
     const uint8_t *abuf = lds + buf * kBufBytes + c16 * kRowBytes;
@@ -462,7 +461,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   // same number in flight and the compiler's wait counts stay exact.
   auto body = [&](int s, const Stage &cur, Stage &nxt) {
     lds_barrier();
-    if (!WX && s > 0 && s < steps && s % kTabSteps == 0) {  // next table chunk
+    if (!WX && !PREP && s > 0 && s < steps && s % kTabSteps == 0) {  // next table chunk
       fill_table(s / kTabSteps);
       lds_barrier();
     }
@@ -474,7 +473,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
   };
 
   Stage b0, b1;
-  if (!WX) fill_table(0);
+  if (!WX && !PREP) fill_table(0);
   load_a(0);
   load_b(b0, 0);
   store_a(0);
