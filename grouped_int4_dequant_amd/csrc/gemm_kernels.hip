@@ -416,6 +416,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
       // expanded weights: inputs past K (the last step's loads were clamped
       // to the row start) contribute zero, as the zero table does below
       if constexpr (WX) return kvalid ? __builtin_bit_cast(h8, st.q[cb][j]) : h8{};
+      else if constexpr (PREP) return rb_rebuild_sub(st.q[cb][j], grp[cb]);
       else return rb_rebuild_g(st.q[cb][j], grp[cb], rbk);
     };
     auto read_a = [&](int j, int rb) -> h8 {
@@ -609,6 +610,9 @@ __device__ __forceinline__ void run_rows(const GemmProblem &P, const Unit &U, ui
   }
 }
 
+// The flag of a problem without a prepared copy.
+__device__ const uint32_t g_flag_off = 0u;
+
 template <int MODE, bool AF16, bool WX, bool CHECK = false>
 __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufBytes];
@@ -618,6 +622,11 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
   const int b = blockIdx.x;
   const bool second = args.nprob > 1 && b >= args.prob[1].wg_begin;
   const GemmProblem P = second ? args.prob[1] : args.prob[0];
+  // the prepared copy's flag, requested first so its latency overlaps the
+  // work list and row-index reads
+  constexpr bool kCanBuf = AF16 && !WX;
+  constexpr bool kCanPrep = kCanBuf && MODE != kStoreC;  // the layer's projections
+  const uint32_t pflag = *(kCanPrep && P.Pq != nullptr ? P.Pflag : &g_flag_off);  // unconditional load
   // Workgroup i runs on XCD i % 8. Consecutive groups of 8 workgroups take 8
   // units (one per XCD); the N-slices of one unit stay on one XCD, so its
   // gathered activation rows are fetched into that XCD's L2 once.
@@ -667,11 +676,10 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
   // half-width items: the same code with half the column blocks per wave
   // (always, for expanded weights: their stages take four times the registers)
   // prepared weights (the host sets Pq only when K is a multiple of the
-  // step), else buffer loads when K is a multiple of the step
-  constexpr bool kCanBuf = AF16 && !WX;
-  constexpr bool kCanPrep = kCanBuf && MODE != kStoreC;  // the layer's projections
+  // step; the projection's flag says whether its scales allowed the
+  // prepared form), else buffer loads when K is a multiple of the step
   const bool buf = kCanBuf && (P.K & (kKStep - 1)) == 0;
-  const bool prep = buf && MODE != kStoreC && P.Pq != nullptr;
+  const bool prep = buf && pflag != 0u;
   if (WX || narrow) {
     if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
     else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, false>(P, U, lds, s_arow, tab);
@@ -760,9 +768,20 @@ __global__ __launch_bounds__(256) void prep_codes_kernel(const uint32_t *q, int 
   pq[i] = v;
 }
 
+__global__ void prep_flag_init_kernel(uint32_t *flag, uint32_t v) { *flag = v; }
+
+// Clears the flag when any scale is outside the range of the one-rounding
+// rebuild (one atomic per wave that holds such a scale).
+__global__ __launch_bounds__(256) void prep_check_kernel(const uint16_t *sc, int64_t n, uint32_t *flag) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool bad = i < n && !prep_scale_ok(__uint_as_float((uint32_t)sc[i] << 16));
+  const uint64_t m = __ballot(bad);
+  if (m != 0ull && (threadIdx.x & 63) == (int)(__ffsll((long long)m) - 1)) atomicAnd(flag, 0u);
+}
+
 // Prepared table: one thread per (expert, slice, group, table column) dword.
 __global__ __launch_bounds__(256) void prep_table_kernel(const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
-                                                         bool swiglu, uint32_t *pt) {
+                                                         bool swiglu, const uint32_t *flag, uint32_t *pt) {
   const int G = K / 64;
   const int64_t per_e = (int64_t)prep_slices(N, swiglu) * G * kPrepCols;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -773,20 +792,29 @@ __global__ __launch_bounds__(256) void prep_table_kernel(const uint16_t *sc, con
   const int t = tg / G, g = tg - t * G;
   const int n = prep_row(t, c, N, swiglu);
   const int64_t gi = (int64_t)e * N * G + (int64_t)n * G + g;
-  pt[i] = n >= 0 ? rb_pack_scale_bias(sc[gi], bi[gi]) : 0u;
+  pt[i] = n >= 0 && *flag != 0u ? rb_pack_sub(sc[gi], bi[gi]) : 0u;
 }
 
 hipError_t launch_prepare(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
-                          bool swiglu, uint8_t *pq, uint32_t *pt, hipStream_t s) {
+                          bool swiglu, uint8_t *pq, uint32_t *pt, uint32_t *flag, hipStream_t s) {
   const int64_t n16 = (int64_t)E * prep_code_bytes(N, K, swiglu) / 16;
   const int64_t nt = (int64_t)E * prep_table_dwords(N, K, swiglu);
+  const int64_t ns = (int64_t)E * N * (K / 64);
+  hipLaunchKernelGGL(prep_flag_init_kernel, dim3(1), dim3(1), 0, s, flag, 1u);
+  if (ns > 0)
+    hipLaunchKernelGGL(prep_check_kernel, dim3((unsigned)ceil_div(ns, 256)), dim3(256), 0, s, sc, ns, flag);
   if (n16 > 0)
     hipLaunchKernelGGL(prep_codes_kernel, dim3((unsigned)ceil_div(n16, 256)), dim3(256), 0, s, q, E, N, K, swiglu,
                        reinterpret_cast<uint4 *>(pq));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nt == 0) return err;
   hipLaunchKernelGGL(prep_table_kernel, dim3((unsigned)ceil_div(nt, 256)), dim3(256), 0, s, sc, bi, E, N, K, swiglu,
-                     pt);
+                     flag, pt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_flag(uint32_t *flag, uint32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(prep_flag_init_kernel, dim3(1), dim3(1), 0, s, flag, v);
   return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ PrepLayout prep_layout(const moe_layer_t *L) {
   const int d = L->d, f = L->f, fs = L->f_sh;
   const int64_t E = L->E;
   PrepLayout p{};
-  int64_t at = 0;
+  int64_t at = kPrepHeader;  // the flags come first
   auto take = [&](int64_t bytes) {
     const int64_t o = at;
     at += round_up(bytes, kAlign);
@@ -139,10 +139,11 @@ PrepLayout prep_layout(const moe_layer_t *L) {
 
 // Point a GEMM problem at the prepared copy of one projection (expert
 // stride from the layout), when the layer has one.
-void use_prep(GemmProblem &p, const moe_layer_t *L, int64_t q_ofs, int64_t t_ofs, int N, int K, bool swiglu,
-              bool per_expert) {
+void use_prep(GemmProblem &p, const moe_layer_t *L, int flag, int64_t q_ofs, int64_t t_ofs, int N, int K,
+              bool swiglu, bool per_expert) {
   if (!L->prep || !prep_supported(L)) return;
   const uint8_t *base = static_cast<const uint8_t *>(L->prep);
+  p.Pflag = reinterpret_cast<const uint32_t *>(base) + flag;
   p.Pq = base + q_ofs;
   p.Pt = reinterpret_cast<const uint32_t *>(base + t_ofs);
   p.pq_estride = per_expert ? prep_code_bytes(N, K, swiglu) : 0;
@@ -446,7 +447,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     GemmProblem &q = gd.prob[0];
     q.A = w.h_sh; q.lda = fs; q.a_row = nullptr;
     q.Wq = L->sh_dn_q; q.Ws = L->sh_dn_s; q.Wb = L->sh_dn_b;
-    use_prep(q, L, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
+    use_prep(q, L, kFlagShDn, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
     q.N = d; q.K = fs;
     q.units = nullptr; q.num_units = nullptr; q.implicit_rows = T; q.unit_rows = opt.shared_unit_rows;
     q.nslices = (int)ceil_div(d, kGemmCols);
@@ -492,7 +493,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = 2 * fs; p.K = d;
     p.Wx = wx ? wx + (int64_t)E * 2 * f * d : nullptr; p.wx_estride = 0;
-    if (!opt.unfused) use_prep(p, L, pl.sh_gu_q, pl.sh_gu_t, 2 * fs, d, true, false);
+    if (!opt.unfused) use_prep(p, L, kFlagShGu, pl.sh_gu_q, pl.sh_gu_t, 2 * fs, d, true, false);
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(fs, hcols);
     p.wg_begin = nwg;
@@ -507,7 +508,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)2 * f * (d / 8); p.ws_estride = (int64_t)2 * f * (d / 64);
     p.N = 2 * f; p.K = d;
     p.Wx = wx; p.wx_estride = (int64_t)2 * f * d;
-    if (!opt.unfused) use_prep(p, L, pl.gu_q, pl.gu_t, 2 * f, d, true, true);
+    if (!opt.unfused) use_prep(p, L, kFlagGu, pl.gu_q, pl.gu_t, 2 * f, d, true, true);
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(f, hcols);
     p.ntail = opt.ntail;
@@ -540,7 +541,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = 0; p.ws_estride = 0;
     p.N = d; p.K = fs;
     p.Wx = wx ? wx + (int64_t)E * d * f : nullptr; p.wx_estride = 0;
-    if (!opt.unfused) use_prep(p, L, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
+    if (!opt.unfused) use_prep(p, L, kFlagShDn, pl.sh_dn_q, pl.sh_dn_t, d, fs, false, false);
     p.units = nullptr; p.num_units = nullptr; p.implicit_rows = T; p.unit_rows = opt.unit_rows;
     p.nslices = (int)ceil_div(d, ocols);
     p.wg_begin = nwg;
@@ -555,7 +556,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     p.wq_estride = (int64_t)d * (f / 8); p.ws_estride = (int64_t)d * (f / 64);
     p.N = d; p.K = f;
     p.Wx = wx; p.wx_estride = (int64_t)d * f;
-    if (!opt.unfused) use_prep(p, L, pl.dn_q, pl.dn_t, d, f, false, true);
+    if (!opt.unfused) use_prep(p, L, kFlagDn, pl.dn_q, pl.dn_t, d, f, false, true);
     p.units = w.units; p.num_units = w.num_units; p.implicit_rows = 0;
     p.nslices = (int)ceil_div(d, ocols);
     p.ntail = opt.ntail > 0 ? kNarrowTailDown : 0;  // ablation forms: no tail
@@ -605,15 +606,22 @@ int moe_prepare_weights(const moe_layer_t *L, void *dst, size_t dst_bytes, hipSt
   uint8_t *b = static_cast<uint8_t *>(dst);
   const int d = L->d, f = L->f, fs = L->f_sh, E = L->E;
   auto tab = [&](int64_t o) { return reinterpret_cast<uint32_t *>(b + o); };
-  st = hip_status(launch_prepare(L->gu_q, L->gu_s, L->gu_b, E, 2 * f, d, true, b + pl.gu_q, tab(pl.gu_t), stream));
+  uint32_t *flags = reinterpret_cast<uint32_t *>(b);
+  st = hip_status(launch_prepare(L->gu_q, L->gu_s, L->gu_b, E, 2 * f, d, true, b + pl.gu_q, tab(pl.gu_t),
+                                 flags + kFlagGu, stream));
   if (st == MOE_OK)
-    st = hip_status(launch_prepare(L->dn_q, L->dn_s, L->dn_b, E, d, f, false, b + pl.dn_q, tab(pl.dn_t), stream));
+    st = hip_status(launch_prepare(L->dn_q, L->dn_s, L->dn_b, E, d, f, false, b + pl.dn_q, tab(pl.dn_t),
+                                   flags + kFlagDn, stream));
   if (st == MOE_OK && fs > 0)
     st = hip_status(launch_prepare(L->sh_gu_q, L->sh_gu_s, L->sh_gu_b, 1, 2 * fs, d, true, b + pl.sh_gu_q,
-                                   tab(pl.sh_gu_t), stream));
+                                   tab(pl.sh_gu_t), flags + kFlagShGu, stream));
   if (st == MOE_OK && fs > 0)
     st = hip_status(launch_prepare(L->sh_dn_q, L->sh_dn_s, L->sh_dn_b, 1, d, fs, false, b + pl.sh_dn_q,
-                                   tab(pl.sh_dn_t), stream));
+                                   tab(pl.sh_dn_t), flags + kFlagShDn, stream));
+  if (st == MOE_OK && fs == 0) {  // no shared expert: its flags read 0
+    st = hip_status(launch_prep_flag(flags + kFlagShGu, 0u, stream));
+    if (st == MOE_OK) st = hip_status(launch_prep_flag(flags + kFlagShDn, 0u, stream));
+  }
   return st;
 }
 

@@ -132,6 +132,7 @@ struct GemmProblem {
   // 128; layout in prep_layout.h)
   const uint8_t *Pq; int64_t pq_estride;   // bytes
   const uint32_t *Pt; int64_t pt_estride;  // dwords
+  const uint32_t *Pflag;                   // the projection's flag: 0 = use Wq/Ws/Wb after all
   // outputs
   float *C; int ldc;          // kStoreC
   uint16_t *H; int ldh;       // kSwiGLU (permuted-run columns), kStoreH (natural columns)
@@ -153,7 +154,9 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, h
 // Prepared copy of one projection's weights for E experts (prep_layout.h):
 // swiglu: rows 0..N/2-1 gate, N/2..N-1 up.
 hipError_t launch_prepare(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int E, int N, int K,
-                          bool swiglu, uint8_t *pq, uint32_t *pt, hipStream_t s);
+                          bool swiglu, uint8_t *pq, uint32_t *pt, uint32_t *flag, hipStream_t s);
+// One flag word of a prepared copy set to v (a kernel, so the call can be captured).
+hipError_t launch_prep_flag(uint32_t *flag, uint32_t v, hipStream_t s);
 // Unfused ablation: weights of rows x K expanded into fp16 (rebuild order).
 hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int64_t rows, int K,
                          uint16_t *out, hipStream_t s);

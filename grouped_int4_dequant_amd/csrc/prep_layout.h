@@ -26,8 +26,15 @@
 // plain: 64 w + 16 b + c.
 //
 // Table, per expert: slice t, then group g (64 inputs, K / 64 groups), then
-// 256 dwords, one per table column: fp16 s in the low half, fp16 (b + 8 s)
-// in the high half, both rounded from the bf16 scale and bias.
+// 256 dwords, one per table column: fp16 (s * 2^20) in the low half and
+// fp16 b in the high half, both exact from the bf16 scale and bias when
+// |s| < 2^-4, the pair of the one-rounding rebuild (rb_rebuild_sub). A
+// projection with any scale outside that range keeps a zero table and its
+// flag (below) at 0, and its GEMM reads the original arrays.
+//
+// Flags: the prepared copy starts with a 256-byte header whose uint32 words
+// 0..3 hold, for the routed gate/up, routed down, shared gate/up and shared
+// down projections, 1 when the projection's prepared form is in use.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,6 +55,16 @@ __host__ __device__ inline int64_t prep_code_bytes(int N, int K, bool swiglu) {
 }
 __host__ __device__ inline int64_t prep_table_dwords(int N, int K, bool swiglu) {
   return (int64_t)prep_slices(N, swiglu) * (K / 64) * kPrepCols;
+}
+
+constexpr int kPrepHeader = 256;   // bytes of the flags header
+enum PrepFlag : int { kFlagGu = 0, kFlagDn = 1, kFlagShGu = 2, kFlagShDn = 3 };
+
+// a scale the one-rounding rebuild takes: 0, or 2^-34 <= |s| < 2^-4 (s * 2^20
+// a normal fp16 that holds all 8 bits of a bf16 scale)
+__host__ __device__ inline bool prep_scale_ok(float s) {
+  const float a = s < 0.f ? -s : s;
+  return a == 0.f || (a >= 5.820766091346741e-11f && a < 0.0625f);
 }
 
 // weight row of table column c (0..255) of slice t, or -1 past the end

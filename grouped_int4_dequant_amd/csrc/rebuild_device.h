@@ -83,6 +83,31 @@ __device__ __forceinline__ rb_h8 rb_rebuild_g(uint32_t w, const RbGroup &g, cons
   return rb_h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
 }
 
+// Eight weights of one code word in one rounding each, from the pair
+// (fp16 s * 2^20, fp16 b) of its group (valid when |s| < 2^-4, so that
+// s * 2^20 is a normal fp16): a code moved to bits 4..7 of an fp16 half with
+// a zero exponent is the subnormal q * 2^-20, exact, and one v_pk_fma_f16
+// forms fp16(q * 2^-20 * s * 2^20 + b) = fp16(s * q + b). Three shifts and
+// four ands place the eight codes, in the same order as rb_rebuild_g.
+__device__ __forceinline__ rb_h8 rb_rebuild_sub(uint32_t w, const RbGroup &g) {
+  const uint32_t m = 0x00F000F0u;
+  const rb_h2 t0 = __builtin_bit_cast(rb_h2, (w << 4) & m);  // (q0, q4)
+  const rb_h2 t1 = __builtin_bit_cast(rb_h2, w & m);         // (q1, q5)
+  const rb_h2 t2 = __builtin_bit_cast(rb_h2, (w >> 4) & m);  // (q2, q6)
+  const rb_h2 t3 = __builtin_bit_cast(rb_h2, (w >> 8) & m);  // (q3, q7)
+  const rb_h2 w0 = __builtin_elementwise_fma(t0, g.s1, g.cc);
+  const rb_h2 w1 = __builtin_elementwise_fma(t1, g.s1, g.cc);
+  const rb_h2 w2 = __builtin_elementwise_fma(t2, g.s1, g.cc);
+  const rb_h2 w3 = __builtin_elementwise_fma(t3, g.s1, g.cc);
+  return rb_h8{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+}
+
+// The pair rb_rebuild_sub takes, from bf16 bits (its caller checks the range).
+__device__ __forceinline__ uint32_t rb_pack_sub(uint32_t s_bits, uint32_t b_bits) {
+  const float sf = __uint_as_float(s_bits << 16) * 1048576.f, bf = __uint_as_float(b_bits << 16);
+  return (uint32_t)__half_as_ushort(__float2half_rn(sf)) | ((uint32_t)__half_as_ushort(__float2half_rn(bf)) << 16);
+}
+
 // Eight weights of one code word; sc = packed (fp16 s, fp16 (b + 8 s)).
 __device__ __forceinline__ rb_h8 rb_rebuild(uint32_t w, uint32_t sc_packed, const RbConsts &k) {
   return rb_rebuild_g(w, rb_group(sc_packed), k);

@@ -86,9 +86,9 @@ extern "C" {
  *   prep  NULL, or a prepared copy of the same weights written by
  *         moe_prepare_weights for this layer (256-byte aligned, kept alive
  *         and unchanged by the caller). When set, the prefill grouped GEMMs
- *         read it instead of the arrays above (same arithmetic, results equal
- *         bit for bit); the few-token form and the ablation forms still read
- *         the arrays, which must stay valid.
+ *         read it instead of the arrays above (see moe_prepare_weights for
+ *         the arithmetic); the few-token form and the ablation forms still
+ *         read the arrays, which must stay valid.
  * All weight pointers must be 16-byte aligned.
  */
 typedef struct moe_layer {
@@ -114,14 +114,22 @@ size_t moe_prepared_bytes(const moe_layer_t *L);
  * set L->prep = dst (the caller does) to have the prefill GEMMs use it.
  * The copy holds the same 4-bit codes rearranged so that one workgroup item
  * of the grouped GEMM reads each 128-input step of its 256 output columns as
- * one contiguous 16 KiB block, and each group's (fp16 s, fp16 (b + 8 s))
- * pair, the constants of the on-chip rebuild, already formed and in the
- * order of the item's LDS table (Lily-EN "Prefill: Keep Weights Packed,
- * Keep Routing on the GPU": the weights stay 4-bit in memory; the layout is
- * this library's). dst then holds, each part starting at a multiple of 256
- * bytes: the routed experts' gate/up codes, their table, the routed down
+ * one contiguous 16 KiB block, and each group's scale and bias as the fp16
+ * pair (s * 2^20, b) in the order of the item's columns, from which one
+ * fused multiply-add per two weights forms fp16(s * q + b) with a single
+ * rounding (Lily-EN "Prefill: Keep Weights Packed, Keep Routing on the
+ * GPU": the weights stay 4-bit in memory; the layout is this library's).
+ * That form needs |s| < 2^-4 (and s = 0 or |s| >= 2^-34); a projection with
+ * any other scale keeps its flag at 0 and its GEMM reads the original
+ * arrays. dst then holds, each part starting at a multiple of 256 bytes: a
+ * header whose uint32 words 0..3 are the flags of the routed gate/up,
+ * routed down, shared gate/up and shared down projections (1: prepared form
+ * in use), the routed experts' gate/up codes, their table, the routed down
  * codes, their table, and (f_sh > 0) the same four parts of the shared
- * expert. One-time work per layer (a few hundred microseconds per GB).
+ * expert. Results equal those of the original arrays bit for bit whenever
+ * b + 8 s is exact in fp16 (as for the synthetic workloads' weights, whose
+ * |b + 8 s| stays below s); otherwise the prepared form is the one that
+ * rounds once. One-time work per layer (a few hundred microseconds per GB).
  * L->prep is ignored. Errors: MOE_EINVAL (invalid layer, null or
  * misaligned dst), MOE_EUNSUPPORTED (d, f or f_sh not a multiple of 128),
  * MOE_EWORKSPACE (dst_bytes too small), MOE_EHIP.

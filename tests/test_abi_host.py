@@ -61,7 +61,8 @@ def test_prepared_bytes():
     MiB = 2 ** 20
     # the same bytes as the weights: codes (1 + 0.5 MiB per expert), one
     # 4-byte pair per group (128 + 64 KiB per expert), and the shared expert's
-    expect = 256 * (MiB + MiB // 2) + 256 * (128 + 64) * 1024 + (MiB + MiB // 2 + 192 * 1024)
+    # (after a 256-byte header of flags)
+    expect = 256 + 256 * (MiB + MiB // 2) + 256 * (128 + 64) * 1024 + (MiB + MiB // 2 + 192 * 1024)
     assert lib.moe_prepared_bytes(ctypes.byref(L)) == expect
     assert lib.moe_prepared_bytes(ctypes.byref(qwen_layer_struct(f_sh=0))) == expect - (MiB + MiB // 2 + 192 * 1024)
     # d, f or f_sh not a multiple of 128: no prepared form

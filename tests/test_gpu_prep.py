@@ -67,13 +67,17 @@ def prep_codes_np(q, N, K, swiglu):
 
 
 def prep_table_np(s_bits, b_bits, N, K, swiglu):
-    """bf16 bits [E][N][K/64] -> packed (fp16 s, fp16 (b + 8 s)) [E][S][G][256]."""
+    """bf16 bits [E][N][K/64] -> packed (fp16 s * 2^20, fp16 b) [E][S][G][256]
+    (the scales here are inside the range of that form)."""
     E, G = s_bits.shape[0], K // 64
-    sf = S.bf16_bits_to_f32(s_bits).astype(np.float32)
-    bf = S.bf16_bits_to_f32(b_bits).astype(np.float32)
-    lo = sf.astype(np.float16).view(np.uint16).astype(np.uint32)
-    hi = (bf + np.float32(8.0) * sf).astype(np.float16).view(np.uint16).astype(np.uint32)
-    packed = lo | (hi << 16)
+    sf = S.bf16_bits_to_f32(s_bits).astype(np.float64)
+    bf = S.bf16_bits_to_f32(b_bits).astype(np.float64)
+    assert np.all(np.abs(sf) < 2.0 ** -4)
+    lo = (sf * 2.0 ** 20).astype(np.float16)
+    assert np.array_equal(lo.astype(np.float64), sf * 2.0 ** 20)  # exact
+    hi = bf.astype(np.float16)
+    assert np.array_equal(hi.astype(np.float64), bf)              # exact
+    packed = lo.view(np.uint16).astype(np.uint32) | (hi.view(np.uint16).astype(np.uint32) << 16)
     S_ = _slices(N, swiglu)
     out = np.zeros((E, S_, G, 256), np.uint32)
     for t in range(S_):
@@ -101,7 +105,9 @@ def test_prepared_bytes_follow_the_layout(moe, d, f, E, f_sh):
                   prep_table_np(L["sh_gu_s"][None], L["sh_gu_b"][None], 2 * f_sh, d, True),
                   prep_codes_np(L["sh_dn_q"][None], d, f_sh, False),
                   prep_table_np(L["sh_dn_s"][None], L["sh_dn_b"][None], d, f_sh, False)]
-    at = 0
+    flags = got[:4]
+    assert flags.tolist() == [1, 1, 1 if f_sh else 0, 1 if f_sh else 0], flags
+    at = 64  # after the 256-byte header of flags
     for i, ref in enumerate(parts):
         ref = ref.reshape(-1)
         assert np.array_equal(got[at:at + ref.size], ref), f"region {i}"
@@ -135,3 +141,27 @@ def test_prepared_equals_unprepared(moe, T, d, f, E, k, f_sh):
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     assert torch.isfinite(y1).all()
+
+
+def test_large_scale_projection_falls_back(moe):
+    """A gate/up scale of 2^-4 or more keeps the gate/up flag at 0 (that GEMM
+    reads the original arrays); the other projections stay prepared; y still
+    equals the unprepared layer's."""
+    T, d, f, E, k, f_sh = 200, 512, 256, 6, 2, 128
+    p = S.make_custom(T, S.LayerShape(d=d, f=f, E=E, k=k, f_sh=f_sh), seed=77)
+    lay = dict(p.layer)
+    gs = lay["gu_s"].copy()
+    gs[2, 5, 1] = S.f32_to_bf16_bits(np.array([0.0625], np.float32))[0]
+    lay["gu_s"] = gs
+    say("large scale in routed gate/up: prepared flags and outputs")
+    plain = moe.Layer.from_numpy(d, f, E, k, f_sh, lay, prepare=False)
+    prep = moe.Layer(d, f, E, k, f_sh, plain.tensors, prepare=True)
+    off = prep.c.prep - prep.prep.data_ptr()
+    flags = prep.prep[off:off + 16].cpu().numpy().view(np.uint32)
+    assert flags.tolist() == [0, 1, 1, 1], flags
+    x = torch.from_numpy(p.x.view(np.int16)).view(torch.bfloat16).cuda()
+    lg = torch.from_numpy(p.logits).cuda()
+    y0 = moe.layer_forward(plain, x, lg)
+    y1 = moe.layer_forward(prep, x, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
