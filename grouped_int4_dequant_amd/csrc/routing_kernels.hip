@@ -24,8 +24,8 @@
 //         gives the stable scatter:
 //           pos = offset[e] + before[e] + popcount(mask[e] & tokens below t).
 //         Integer atomics commute, so the result is deterministic.
-//         One more workgroup writes counts, offsets, the 32-row block map and
-//         the GEMM work list.
+//         One more workgroup writes counts, offsets and the 32-row block
+//         map, and (for the layer) another one the GEMM work list.
 //
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -218,12 +218,54 @@ __global__ __launch_bounds__(kThreads) void count_kernel(ScanArgs a) {
   for (int e = threadIdx.x; e < E; e += kThreads) a.chunk_counts[(int64_t)c * E + e] = s_cnt[e];
 }
 
+// GEMM work list (one workgroup): each expert's rows split evenly into
+// ceil(rows / unit_rows) units, listed by 16-row size class, largest first,
+// so the GEMM (which hands units to workgroups in list order) starts the
+// longest ones first. The order within a class follows LDS atomics; it
+// changes which workgroup runs a unit, never a result.
+__device__ void write_units(const ScanArgs &a, const int *s_tot, const int *s_off) {
+  const int E = a.E;
+  __shared__ int s_cls[kClasses + 1];
+  if (threadIdx.x <= kClasses) s_cls[threadIdx.x] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
+    for (int u = 0; u < nu; ++u) {
+      const int rows = (int)((int64_t)(u + 1) * tot / nu) - (int)((int64_t)u * tot / nu);
+      atomicAdd(&s_cls[kClasses - (rows + 15) / 16], 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i <= kClasses; ++i) {
+      const int n = s_cls[i];
+      s_cls[i] = run;
+      run += n;
+    }
+    *a.num_units = run;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
+    for (int u = 0; u < nu; ++u) {
+      const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
+      const int slot = atomicAdd(&s_cls[kClasses - (b1 - b0 + 15) / 16], 1);
+      int32_t *ent = a.units + 3 * (int64_t)slot;
+      ent[0] = e;
+      ent[1] = s_off[e] + b0;
+      ent[2] = b1 - b0;
+    }
+  }
+}
+
 // Per sub-chunk c: expert totals and the counts of the sub-chunks before c
 // (counted here, or column sums of cnt), offsets by an exclusive scan over experts, and the
 // stable scatter of c's pairs:
 //   pos = offset[e] + before[e] + popcount(mask[e] & tokens of c below t).
-// One extra workgroup (the last, with no pairs of its own) writes counts,
-// offsets, the 32-row block map and the GEMM work list meanwhile.
+// Workgroup C (with no pairs of its own) writes counts, offsets and the
+// 32-row block map meanwhile, and workgroup C + 1 (launched with a work list)
+// the GEMM work list.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
@@ -232,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ int s_scratch[kWaves];
   const int E = a.E, k = a.k, T = a.T;
-  const int c = blockIdx.x, C = gridDim.x - 1;  // sub-chunks; workgroup C holds none
+  const int c = blockIdx.x, C = (int)((T + kSubChunk - 1) / kSubChunk);  // sub-chunks; workgroups C, C + 1 hold none
   const int64_t tk = (int64_t)T * k;
   const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
 
@@ -320,10 +362,14 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
     a.sorted_token[pos] = t;
     a.pair_pos[idx] = pos;
   }
-  if (c != C) return;
+  if (c < C) return;
+  if (c == C + 1) {  // with a work list: a second extra workgroup writes it
+    write_units(a, s_tot, s_off);
+    return;
+  }
 
-  // the last workgroup (which holds no pairs): counts, offsets, block map and
-  // GEMM work list, beside the scatter of the others
+  // the first extra workgroup (neither holds pairs): counts, offsets and the
+  // block map, beside the scatter of the others
   for (int e = threadIdx.x; e < E; e += kThreads) {
     a.counts[e] = s_tot[e];
     a.offsets[e] = s_off[e];
@@ -347,45 +393,6 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
     a.block_map[3 * (int64_t)i + 2] = 0;
   }
   if (threadIdx.x == 0) *a.num_blocks = nblocks;
-  if (a.units == nullptr) return;
-  __syncthreads();
-  // Work list: each expert's rows split evenly into ceil(rows / unit_rows)
-  // units, listed by 16-row size class, largest first, so the GEMM (which
-  // hands units to workgroups in list order) starts the longest ones first.
-  // The order within a class follows LDS atomics; it changes which
-  // workgroup runs a unit, never a result.
-  __shared__ int s_cls[kClasses + 1];
-  if (threadIdx.x <= kClasses) s_cls[threadIdx.x] = 0;
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
-    for (int u = 0; u < nu; ++u) {
-      const int rows = (int)((int64_t)(u + 1) * tot / nu) - (int)((int64_t)u * tot / nu);
-      atomicAdd(&s_cls[kClasses - (rows + 15) / 16], 1);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i <= kClasses; ++i) {
-      const int n = s_cls[i];
-      s_cls[i] = run;
-      run += n;
-    }
-    *a.num_units = run;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
-    for (int u = 0; u < nu; ++u) {
-      const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
-      const int slot = atomicAdd(&s_cls[kClasses - (b1 - b0 + 15) / 16], 1);
-      int32_t *ent = a.units + 3 * (int64_t)slot;
-      ent[0] = e;
-      ent[1] = s_off[e] + b0;
-      ent[2] = b1 - b0;
-    }
-  }
 }
 
 }  // namespace
@@ -426,8 +433,9 @@ hipError_t launch_scan(const ScanArgs &args, hipStream_t s, hipEvent_t stop) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // one workgroup per sub-chunk, plus one for the block map and work list
-  hipExtLaunchKernelGGL(scatter_kernel, dim3(C + 1), dim3(kThreads), 0, s, nullptr, stop, 0, a);
+  // one workgroup per sub-chunk, plus one for the block map and one for the
+  // work list
+  hipExtLaunchKernelGGL(scatter_kernel, dim3(C + 1 + (a.units ? 1 : 0)), dim3(kThreads), 0, s, nullptr, stop, 0, a);
   return hipGetLastError();
 }
 
