@@ -81,6 +81,7 @@ struct ScanArgs {
   int unit_rows;                // rows per GEMM work unit at most (16..kUnitRows)
   int32_t *chunk_counts;        // scratch [ceil(T/64)][E] (two-pass form only)
   int count_inline;             // set by launch_scan: the scatter workgroups count every pair themselves
+  int ids_vec;                  // set by launch_scan: topk_ids 16-byte aligned and T*k a multiple of 4
 };
 
 // logits[t][e] = sum_k x[t][k] * w[e][k] (bf16 inputs, fp32 accumulation).
