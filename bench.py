@@ -37,11 +37,13 @@ METRIC = "MoE-layer prefill tokens/s @T=2048 (% MFMA peak); T=1 HBM GB/s (% peak
 # describe the kernels built from the sources with this digest; after any change
 # to those sources the figure is stale and reported as null.
 TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
+                   "grouped_int4_dequant_amd/csrc/prep_layout.h",
+                   "grouped_int4_dequant_amd/csrc/rebuild_device.h",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "b62d8d2ead83f75c16af3f32b3338e3fbb65219fa70354e8787e4636ee83ee01"
-TRAFFIC_BYTES = {"gate_up": (208487.5 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85645.3 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.9) * 1024}
+TRAFFIC_DIGEST = "5d9622bf5af285cbd81e2f2ef7b7eb23df427909a640e34f381c79eb326c10f5"
+TRAFFIC_BYTES = {"gate_up": (185357.0 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85509.6 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
 
 
 def sources_digest():
