@@ -610,6 +610,29 @@ __device__ __forceinline__ void run_rows(const GemmProblem &P, const Unit &U, ui
   }
 }
 
+// One item (at most kUnitRows rows): the row indices to LDS, then the
+// compiled form for its width, weight source and row-block count.
+template <int MODE, bool AF16, bool WX, bool CHECK, bool kCanBuf, bool kCanPrep>
+__device__ __forceinline__ void run_item(const GemmProblem &P, const Unit &U, uint8_t *lds, int *s_arow,
+                                         uint32_t *tab, bool buf, bool prep, bool narrow) {
+  for (int r = threadIdx.x; r < kUnitRows; r += kGemmThreads) {
+    const int p = U.r0 + min(r, U.nr - 1);
+    s_arow[r] = P.a_row ? P.a_row[p] : p;
+  }
+  __syncthreads();
+  // half-width items: the same code with half the column blocks per wave
+  // (always, for expanded weights: their stages take four times the registers)
+  if (WX || narrow) {
+    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
+    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, false>(P, U, lds, s_arow, tab);
+    else          run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, false, false>(P, U, lds, s_arow, tab);
+  } else {
+    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
+    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, false>(P, U, lds, s_arow, tab);
+    else          run_rows<MODE, AF16, WX, CHECK, kCBFull, false, false>(P, U, lds, s_arow, tab);
+  }
+}
+
 // The flag of a problem without a prepared copy.
 __device__ const uint32_t g_flag_off = 0u;
 
@@ -655,7 +678,7 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
     const int32_t *u = P.units + 3 * (int64_t)unit;
     U.e = u[0];
     U.r0 = u[1];
-    U.nr = min(u[2], kUnitRows);
+    U.nr = u[2];
   } else {
     const int slot = lb >> 3;
     unit = (slot / nsl) * 8 + (lb & 7);
@@ -667,28 +690,19 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
     if (U.nr <= 0) return;
   }
 
-  for (int r = threadIdx.x; r < kUnitRows; r += kGemmThreads) {
-    const int p = U.r0 + min(r, U.nr - 1);
-    s_arow[r] = P.a_row ? P.a_row[p] : p;
-  }
-  __syncthreads();
-
-  // half-width items: the same code with half the column blocks per wave
-  // (always, for expanded weights: their stages take four times the registers)
   // prepared weights (the host sets Pq only when K is a multiple of the
   // step; the projection's flag says whether its scales allowed the
   // prepared form), else buffer loads when K is a multiple of the step
   const bool buf = kCanBuf && (P.K & (kKStep - 1)) == 0;
   const bool prep = buf && pflag != 0u;
-  if (WX || narrow) {
-    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
-    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, kCanBuf, false>(P, U, lds, s_arow, tab);
-    else          run_rows<MODE, AF16, WX, CHECK, kCBFull / 2, false, false>(P, U, lds, s_arow, tab);
-  } else {
-    if (prep)     run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab);
-    else if (buf) run_rows<MODE, AF16, WX, CHECK, kCBFull, kCanBuf, false>(P, U, lds, s_arow, tab);
-    else          run_rows<MODE, AF16, WX, CHECK, kCBFull, false, false>(P, U, lds, s_arow, tab);
-  }
+  // A unit has at most kUnitRows rows: the layer's lists by construction; a
+  // caller's block map for the stand-alone GEMM by contract (blocks of 1..32
+  // rows), and of a longer block only its first kUnitRows rows are computed.
+  // (A loop over pieces of a long block around the item made the compiler
+  // spill the item's registers and move code into called functions.)
+  if (U.nr <= 0) return;
+  U.nr = min(U.nr, kUnitRows);
+  run_item<MODE, AF16, WX, CHECK, kCanBuf, kCanPrep>(P, U, lds, s_arow, tab, buf, prep, narrow);
 }
 
 }  // namespace

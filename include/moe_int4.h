@@ -258,8 +258,9 @@ int moe_layer_forward_router(const moe_layer_t *L, const uint16_t *x, const uint
  * Errors: MOE_EINVAL (null, unaligned ws, T < 0, k < 1, k > E),
  * MOE_EUNSUPPORTED (E > 1024, k > 64, T > MOE_MAX_CALL_TOKENS),
  * MOE_EWORKSPACE (ws_bytes too small). T == 0 enqueues nothing. Launches
- * three kernels (top-k; per-64-token expert counts; offsets, stable scatter
- * and block map).
+ * two kernels (top-k; expert counts, offsets, stable scatter and block map),
+ * and above 32768 (token, slot) pairs a per-64-token count pass between
+ * them.
  */
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
               const moe_routing_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -278,8 +279,11 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
  *   block_map int32 [max_blocks][3] as produced by moe_route; num_blocks [1]
  *   C         fp32 [*][ldc]; rows not covered by a block are not written
  * N and K must be multiples of 64 (else MOE_EUNSUPPORTED, as is N * K / 8
- * reaching 2^31); every block has 1..32 rows (the block map contract; longer
- * blocks are cut at 96 rows). Each block is one work unit of the kernel.
+ * reaching 2^31). The block map contract gives every block 1..32 rows, and
+ * each block is one work unit of the kernel. Of a longer block (a caller's
+ * own map) only the first 96 rows are computed; the C rows past them keep
+ * their contents, as do those of a block of zero or fewer rows (nothing is
+ * checked on the host: the map lives on the device).
  */
 int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
                           int32_t N, int32_t K,
@@ -294,8 +298,9 @@ int moe_grouped_gemm_int4(const uint16_t *A, int32_t lda, const int32_t *a_row,
  * routing: optional (may be NULL); when given, it receives the routing
  * tensors of this call. ws: device workspace of at least
  * moe_workspace_bytes(T, L) bytes, 256-byte aligned. Never synchronises.
- * Prefill enqueues six kernels (top-k, per-64-token counts, scan/scatter,
- * gate-up, down, combine). Calls of at most 8 tokens with d a multiple of
+ * Prefill enqueues five kernels (top-k, counts/scan/scatter, gate-up, down,
+ * combine; six above 32768 (token, slot) pairs, with a per-64-token count
+ * pass). Calls of at most 8 tokens with d a multiple of
  * 512, f == 512 and f_sh in {0, 512} take the decode form instead: two
  * kernels (gate-up with the top-k repeated in each workgroup; down with
  * the combine), plus the routing kernels only when routing is requested

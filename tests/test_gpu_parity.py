@@ -155,6 +155,44 @@ def test_grouped_gemm_matches_oracle(moe, N, K, E, k, T):
     check_output(Cg, ref, "grouped gemm")
 
 
+def test_grouped_gemm_long_and_empty_blocks(moe):
+    """Outside the block map contract (1..32 rows per block): of a block
+    longer than the 96-row work unit only the first 96 rows are computed,
+    and empty or negative blocks write nothing; every other row keeps its
+    old contents."""
+    N, K, E = 256, 512, 3
+    say("grouped gemm with blocks of 200, 97, 96, 1, 0 and -5 rows")
+    rng = np.random.default_rng(11)
+    Wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint32)
+    Ws = S.f32_to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 64)).astype(np.float32))
+    Wb = S.f32_to_bf16_bits((-8 * O.bf16_value(Ws) * (1 + rng.uniform(-0.1, 0.1, Ws.shape))).astype(np.float32))
+    rows = 420
+    A = S.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    a_row = rng.permutation(rows).astype(np.int32)
+    # (expert, first row, rows); rows 394..399 are in no block
+    blocks = np.array([[0, 0, 200], [2, 200, 97], [1, 297, 96], [2, 393, 1], [1, 400, 0], [0, 400, -5],
+                       [1, 400, 20]], np.int32)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).cuda()
+    C = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm_int4(dev(A, np.int16).view(torch.bfloat16), dev(a_row, np.int32), N, K,
+                          dev(Wq, np.int32), dev(Ws, np.int16).view(torch.bfloat16),
+                          dev(Wb, np.int16).view(torch.bfloat16), dev(blocks, np.int32),
+                          dev(np.array([len(blocks)], np.int32), np.int32), C)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    X = O.bf16_value(A)
+    covered = np.zeros(rows, bool)
+    for e, r0, n in blocks:
+        n = min(n, 96)
+        if n <= 0:
+            continue
+        W = O.dequant(Wq[e], Ws[e], Wb[e])
+        ref = X[a_row[r0:r0 + n]] @ W.T
+        check_output(Cg[r0:r0 + n], ref, f"block ({e}, {r0}, {n})")
+        covered[r0:r0 + n] = True
+    assert np.isnan(Cg[~covered]).all()
+
+
 # ------------------------------------------------------------------ layer
 def test_layer_config0(moe):
     p = S.make_problem(0)
