@@ -40,10 +40,11 @@ TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/prep_layout.h",
                    "grouped_int4_dequant_amd/csrc/rebuild_device.h",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
-                   "grouped_int4_dequant_amd/csrc/moe_api.hip")
-TRAFFIC_DIGEST = "5d9622bf5af285cbd81e2f2ef7b7eb23df427909a640e34f381c79eb326c10f5"
-TRAFFIC_BYTES = {"gate_up": (185357.0 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85509.6 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
+                   "grouped_int4_dequant_amd/csrc/moe_api.hip",
+                   "grouped_int4_dequant_amd/csrc/routing_kernels.hip")
+TRAFFIC_DIGEST = "46dbc3a4d1f6f9b2b301efc04e9a6fbf2861b1988ae276574a8a93308d6fe0a9"
+TRAFFIC_BYTES = {"gate_up": (185639.0 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85496.6 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
 
 
 def sources_digest():
