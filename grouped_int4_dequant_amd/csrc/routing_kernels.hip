@@ -241,45 +241,80 @@ __device__ __forceinline__ void count_ids4(const int32_t *ids, int64_t n4, int64
   }
 }
 
-// GEMM work list (one workgroup): each expert's rows split evenly into
-// ceil(rows / unit_rows) units, listed by 16-row size class, largest first,
+// GEMM work list (one workgroup): each expert's rows split into
+// ceil(rows / unit_rows) units whose sizes differ by at most one, listed by 16-row size class, largest first,
 // so the GEMM (which hands units to workgroups in list order) starts the
-// longest ones first. The order within a class follows LDS atomics; it
-// changes which workgroup runs a unit, never a result.
+// longest ones first. Positions come from ballots: each wave counts its
+// units per class, and a unit's place within its class is (earlier waves'
+// units of the class, earlier rounds of this wave, lanes below it in this
+// round). Expert e is thread e % kThreads's round e / kThreads (then one
+// round per further unit), so the list is the same on every call. Only
+// 32-bit arithmetic: a 64-bit division per unit cost about a microsecond
+// on this workgroup, which finishes last.
 __device__ void write_units(const ScanArgs &a, const int *s_tot, const int *s_off) {
-  const int E = a.E;
-  __shared__ int s_cls[kClasses + 1];
-  if (threadIdx.x <= kClasses) s_cls[threadIdx.x] = 0;
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
-    for (int u = 0; u < nu; ++u) {
-      const int rows = (int)((int64_t)(u + 1) * tot / nu) - (int)((int64_t)u * tot / nu);
-      atomicAdd(&s_cls[kClasses - (rows + 15) / 16], 1);
+  const int E = a.E, ur = a.unit_rows;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ int s_wcnt[kWaves][kClasses + 1];
+  __shared__ int s_base[kWaves][kClasses + 1];
+  // visits every unit of this thread's experts in a wave-uniform order;
+  // f(class, or -1 when this lane has no unit in the round; rows; expert; first row)
+  auto rounds = [&](auto &&f) {
+    for (int e0 = 0; e0 < E; e0 += kThreads) {
+      const int e = e0 + threadIdx.x;
+      const int tot = e < E ? s_tot[e] : 0, nu = (tot + ur - 1) / ur;
+      // q rows per unit, the first rr units one more (32-bit arithmetic only)
+      const int q = nu > 0 ? tot / nu : 0, rr = tot - q * nu;
+      for (int u = 0; __ballot(u < nu) != 0ull; ++u) {
+        int cls = -1, b0 = 0, rows = 0;
+        if (u < nu) {
+          b0 = u * q + min(u, rr);
+          rows = q + (u < rr ? 1 : 0);
+          cls = kClasses - (rows + 15) / 16;
+        }
+        f(cls, rows, e, b0);
+      }
     }
+  };
+  int cnt[kClasses + 1];
+#pragma unroll
+  for (int c = 0; c <= kClasses; ++c) cnt[c] = 0;
+  rounds([&](int cls, int, int, int) {
+#pragma unroll
+    for (int c = 0; c <= kClasses; ++c) cnt[c] += (int)__popcll(__ballot(cls == c));
+  });
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c <= kClasses; ++c) s_wcnt[wave][c] = cnt[c];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int run = 0;
-    for (int i = 0; i <= kClasses; ++i) {
-      const int n = s_cls[i];
-      s_cls[i] = run;
-      run += n;
-    }
+    for (int c = 0; c <= kClasses; ++c)
+      for (int w = 0; w < kWaves; ++w) {
+        s_base[w][c] = run;
+        run += s_wcnt[w][c];
+      }
     *a.num_units = run;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int tot = s_tot[e], nu = (tot + a.unit_rows - 1) / a.unit_rows;
-    for (int u = 0; u < nu; ++u) {
-      const int b0 = (int)((int64_t)u * tot / nu), b1 = (int)((int64_t)(u + 1) * tot / nu);
-      const int slot = atomicAdd(&s_cls[kClasses - (b1 - b0 + 15) / 16], 1);
+#pragma unroll
+  for (int c = 0; c <= kClasses; ++c) cnt[c] = s_base[wave][c];
+  rounds([&](int cls, int rows, int e, int b0) {
+    int slot = 0;
+#pragma unroll
+    for (int c = 0; c <= kClasses; ++c) {
+      const uint64_t m = __ballot(cls == c);
+      if (cls == c)
+        slot = cnt[c] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      cnt[c] += (int)__popcll(m);
+    }
+    if (cls >= 0) {
       int32_t *ent = a.units + 3 * (int64_t)slot;
       ent[0] = e;
       ent[1] = s_off[e] + b0;
-      ent[2] = b1 - b0;
+      ent[2] = rows;
     }
-  }
+  });
 }
 
 // Per sub-chunk c: expert totals and the counts of the sub-chunks before c
@@ -298,8 +333,21 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   __shared__ int s_scratch[kWaves];
   const int E = a.E, k = a.k, T = a.T;
   const int c = blockIdx.x, C = (int)((T + kSubChunk - 1) / kSubChunk);  // sub-chunks; workgroups C, C + 1 hold none
-  const int64_t tk = (int64_t)T * k;
-  const int64_t lo = (int64_t)c * kSubChunk * k, hi = min(tk, lo + (int64_t)kSubChunk * k);
+  // pair indices fit 32 bits (T * k <= MOE_MAX_CALL_TOKENS * 64)
+  const int tk = T * k;
+  const int lo = c * kSubChunk * k, hi = min(tk, lo + kSubChunk * k);
+  // this thread's pairs lo + tid + u * kThreads are (token tl, slot rm) of
+  // the sub-chunk, stepped without a division per pair
+  const int kq = kThreads / k, kr = kThreads - kq * k;
+  const int tl0 = (int)threadIdx.x / k, rm0 = (int)threadIdx.x - tl0 * k;
+  auto step = [&](int &tl, int &rm) {
+    tl += kq;
+    rm += kr;
+    if (rm >= k) {
+      rm -= k;
+      ++tl;
+    }
+  };
 
   // The first kIdCache ids of this thread's pairs (lo + tid + u * kThreads)
   // are requested first and kept for both passes below; every load here is
@@ -308,9 +356,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   int idc[kIdCache];
   if (c < C) {
 #pragma unroll
-    for (int u = 0; u < kIdCache; ++u) idc[u] = a.topk_ids[min(lo + threadIdx.x + (int64_t)u * kThreads, hi - 1)];
+    for (int u = 0; u < kIdCache; ++u) idc[u] = a.topk_ids[min(lo + (int)threadIdx.x + u * kThreads, hi - 1)];
   }
-  auto pair_id = [&](int u, int64_t idx) -> int {
+  auto pair_id = [&](int u, int idx) -> int {
     int id = 0;
 #pragma unroll
     for (int q = 0; q < kIdCache; ++q)
@@ -333,16 +381,16 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
       // ids per load, sixteen loads per thread in flight (lo is a multiple
       // of 64, so the four ids of a load fall on one side of it); up to 4096
       // pairs the one-id loads below were faster (7.4 against 8.0 us at T=512)
-      count_ids4<16>(a.topk_ids, tk >> 2, lo >> 2, s_pre, s_aux);
+      count_ids4<16>(a.topk_ids, (int64_t)(tk >> 2), (int64_t)(lo >> 2), s_pre, s_aux);
     } else {
       constexpr int kBatch = 32;
-      for (int64_t b0 = threadIdx.x; b0 < tk; b0 += (int64_t)kBatch * kThreads) {
+      for (int b0 = threadIdx.x; b0 < tk; b0 += kBatch * kThreads) {
         int v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = a.topk_ids[min(b0 + (int64_t)u * kThreads, tk - 1)];
+        for (int u = 0; u < kBatch; ++u) v[u] = a.topk_ids[min(b0 + u * kThreads, tk - 1)];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int64_t idx = b0 + (int64_t)u * kThreads;
+          const int idx = b0 + u * kThreads;
           if (idx < tk) atomicAdd(idx < lo ? &s_pre[v[u]] : &s_aux[v[u]], 1);
         }
       }
@@ -374,22 +422,21 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
   }
   __syncthreads();
   {
-    int u = 0;
-    for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads, ++u)
-      atomicOr(&s_mask[pair_id(u, idx)], 1ull << (int)(idx / k - (int64_t)c * kSubChunk));
+    int u = 0, tl = tl0, rm = rm0;
+    for (int idx = lo + (int)threadIdx.x; idx < hi; idx += kThreads, ++u, step(tl, rm))
+      atomicOr(&s_mask[pair_id(u, idx)], 1ull << tl);
   }
   const int total = block_exclusive_scan(s_off, E, s_scratch);  // == T*k (syncs inside)
 
   // stable scatter of this sub-chunk's (token, slot) pairs
-  int u = 0;
-  for (int64_t idx = lo + threadIdx.x; idx < hi; idx += kThreads, ++u) {
-    const int t = (int)(idx / k);
-    const int tl = t - c * kSubChunk;
+  int u = 0, tl = tl0, rm = rm0;
+  for (int idx = lo + (int)threadIdx.x; idx < hi; idx += kThreads, ++u, step(tl, rm)) {
+    const int t = c * kSubChunk + tl;
     const int e = pair_id(u, idx);
     const uint64_t m = s_mask[e];
     const uint64_t below = tl == 0 ? 0ull : (m & ((1ull << tl) - 1ull));
     const int pos = s_off[e] + s_pre[e] + __popcll(below);
-    a.sorted_pair[pos] = (int)idx;
+    a.sorted_pair[pos] = idx;
     a.sorted_token[pos] = t;
     a.pair_pos[idx] = pos;
   }

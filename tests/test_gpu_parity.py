@@ -83,6 +83,17 @@ def _adversarial_cases():
     # exact ties including +-0.0
     L = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(100, 8))
     cases.append(("ties", L, 3))
+    # ties at the k-th pick among many lanes and all four 64-expert rows of a
+    # wave: half-step logits, whole rows of +-0.0, and k from 1 to 16
+    L = np.round(rng.standard_normal((96, 256)).astype(np.float32) * 2.0) / 2.0
+    L[::7] = 0.0
+    L[::7, 1::3] = -0.0
+    for kk in (1, 8, 13, 16):
+        cases.append((f"ties_E256_k{kk}", L, kk))
+    L = np.round(rng.standard_normal((64, 1024)).astype(np.float32) * 4.0) / 4.0
+    cases.append(("ties_E1024", L, 8))
+    # every logit equal: the k lowest expert indices
+    cases.append(("all_equal", np.full((10, 200), 0.25, np.float32), 11))
     # all tokens on the same experts
     L = rng.standard_normal((130, 16)).astype(np.float32)
     L[:, :4] += 100.0
@@ -322,14 +333,16 @@ def test_decode_shapes(moe, T, E, k, f_sh, with_routing):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"decode T={T} E={E} k={k}")
 
 
-def test_decode_tied_logits(moe):
+@pytest.mark.parametrize("T,zero_row", [(4, 1), (1, None), (1, 0)])
+def test_decode_tied_logits(moe, T, zero_row):
     """Exact ties (and -0.0 against +0.0) decide which experts the decode
     kernels' own top-k picks; a wrong tie rule changes y by a whole expert."""
-    p = S.make_custom(4, S.LayerShape(d=2048, f=512, E=256, k=8, f_sh=512), seed=77)
+    p = S.make_custom(T, S.LayerShape(d=2048, f=512, E=256, k=8, f_sh=512), seed=77)
     p.logits[:] = np.round(p.logits * 2.0) / 2.0
-    p.logits[1, :] = 0.0
-    p.logits[1, 1::3] = -0.0
-    say("decode tied logits")
+    if zero_row is not None:
+        p.logits[zero_row, :] = 0.0
+        p.logits[zero_row, 1::3] = -0.0
+    say(f"decode tied logits T={T} zero row {zero_row}")
     y, _ = run_layer(moe, p, with_routing=False)
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, 8), "decode ties")
 
