@@ -45,6 +45,7 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 constexpr int kSpan = 512;          // inputs per wave
 constexpr int kSteps = kSpan / 128;  // 128-input steps per wave
 constexpr int kMaxWaves = 8;         // gate/up waves per workgroup (d <= 4096)
+constexpr int kDnResident = 768;      // down workgroups resident at once (3 per CU)
 
 // Position of the r-th set bit of m (r < popcount(m)).
 __device__ __forceinline__ int nth_bit(uint32_t m, int r) {
@@ -72,15 +73,17 @@ __device__ __forceinline__ uint4 x_chunk_h8(uint4 v) {
 }
 
 // ONE: calls of one token (T == 1), whose k picks are the distinct experts.
+// Several tokens with up to 512 experts: five waves per SIMD (every T = 4
+// workgroup resident at once); the one-token and 1024-expert forms keep
+// their registers.
 template <int VPL, bool ONE>
-__global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void decode_gu_kernel(DecodeArgs a) {
   __shared__ int s_ids[kDecodeMaxPairs];
   __shared__ uint32_t s_bits[MOE_MAX_EXPERTS / 32];
   __shared__ int s_uexp[kDecodeMaxPairs];
   __shared__ uint32_t s_umask[kDecodeMaxPairs];
   __shared__ int8_t s_uslot[kDecodeMaxPairs][kDecodeMaxT];  // slot of token t's pick of distinct expert u
   __shared__ int s_U;
-  __shared__ float s_red[kMaxWaves][2][256];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
@@ -94,7 +97,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   // thread's chunk is requested first, so its latency hides behind the
   // routing. Several tokens: the chunks are copied after the weight requests
   // below, so none is held in registers across the top-k.
+  // dynamic LDS: the call's activations, then the waves' partial sums
   extern __shared__ uint4 s_x[];  // [T * d / 8]
+  float(*s_red)[2][256] = reinterpret_cast<float(*)[2][256]>(s_x + T * (a.d / 8));  // [waves][2][256]
   uint4 xr0 = make_uint4(0u, 0u, 0u, 0u);
   if (ONE) xr0 = reinterpret_cast<const uint4 *>(a.x)[tid];
 
@@ -219,26 +224,42 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   __syncthreads();
   const int tok = nth_bit(mask, c16 < nrows ? c16 : 0);
   const uint4 *xl = s_x + ((int64_t)tok * d + kbase + 32 * kq) / 8;
-  u4v xv[kSteps][4];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 v = xl[16 * s + j];
-      xv[s][j] = u4v{v.x, v.y, v.z, v.w};
-    }
 
-  // ---- MFMAs over this wave's inputs
+  // ---- MFMAs over this wave's inputs. One token (288 workgroups, all
+  // resident): every activation fragment is read from LDS up front. Several
+  // tokens: step by step, since holding all of them took 64 registers and
+  // kept the kernel at three waves per SIMD, too few for T = 4's workgroups
+  // to be resident at once.
+  u4v xall[ONE ? kSteps : 1][4];
+  if constexpr (ONE) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = xl[16 * s + j];
+        xall[s][j] = u4v{v.x, v.y, v.z, v.w};
+      }
+  }
   const RbConsts kc = rb_consts();
   f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
+    u4v xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (ONE) {
+        xv[j] = xall[s][j];
+      } else {
+        const uint4 v = xl[16 * s + j];
+        xv[j] = u4v{v.x, v.y, v.z, v.w};
+      }
+    }
     uint32_t sc[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) sc[cb] = group_consts(sw[cb], bw[cb], s, kq >> 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const rb_h8 af = __builtin_bit_cast(rb_h8, xv[s][j]);
+      const rb_h8 af = __builtin_bit_cast(rb_h8, xv[j]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, rb_rebuild(code[cb][s][j], sc[cb], kc), acc[cb], 0,
@@ -276,11 +297,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_gu_kernel(DecodeArgs a)
   }
 }
 
+// NT: tiles of 8 output columns per workgroup (one tile: each slot wave's
+// 16x16 MFMA tile as above; NT tiles: the wave repeats it for NT column
+// groups, each output column computed exactly as with one tile).
+template <int NT>
 __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeArgs a) {
-  __shared__ float s_part[kDecodeMaxSlots][16];
+  __shared__ float s_part[kDecodeMaxSlots][16 * NT];
   __shared__ float s_gate[kDecodeMaxSlots];
   const int tid = threadIdx.x, lane = tid & 63, j = tid >> 6;  // wave j: slot j (j == k: shared)
-  const int k = a.k, d = a.d, blocks = d / 8;
+  const int k = a.k, d = a.d, blocks = d / (8 * NT);
   const int t = blockIdx.x / blocks, cc = blockIdx.x - t * blocks;
   const int c16 = lane & 15, kq = lane >> 4;
   const bool shared = j == k;
@@ -304,44 +329,53 @@ __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeA
       const uint4 v = hs[16 * s + q];
       hv[s][q] = u4v{v.x, v.y, v.z, v.w};
     }
-  // B operand: tile column c16 is output column 8 cc + (c16 & 7) over the
-  // input half c16 >> 3
+  // B operand of tile p: tile column c16 is output column 8 (NT cc + p) +
+  // (c16 & 7) over the input half c16 >> 3
   const bool use_sh = shared && live;
   const int e = shared ? 0 : e_slot;
   const uint32_t *wq = use_sh ? a.sh_dn_q : a.dn_q + (int64_t)e * a.dn_qs;
   const uint16_t *wsc = use_sh ? a.sh_dn_s : a.dn_s + (int64_t)e * a.dn_ss;
   const uint16_t *wbi = use_sh ? a.sh_dn_b : a.dn_b + (int64_t)e * a.dn_ss;
-  const int n = 8 * cc + (c16 & 7), kh = c16 >> 3;
-  const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + (kSpan / 16) * kh + 4 * kq;
-  u4v code[kSteps / 2];
+  const int kh = c16 >> 3;
+  u4v code[NT][kSteps / 2];
+  uint2 sw[NT], bw[NT];
 #pragma unroll
-  for (int s = 0; s < kSteps / 2; ++s) code[s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
-  // the four groups of this half: group 2 s + (kq >> 1) of them feeds step s
-  const uint2 sw = *reinterpret_cast<const uint2 *>(wsc + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
-  const uint2 bw = *reinterpret_cast<const uint2 *>(wbi + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
+  for (int p = 0; p < NT; ++p) {
+    const int n = 8 * (NT * cc + p) + (c16 & 7);
+    const uint32_t *cr = wq + (int64_t)n * (kSpan / 8) + (kSpan / 16) * kh + 4 * kq;
+#pragma unroll
+    for (int s = 0; s < kSteps / 2; ++s) code[p][s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
+    // the four groups of this half: group 2 s + (kq >> 1) of them feeds step s
+    sw[p] = *reinterpret_cast<const uint2 *>(wsc + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
+    bw[p] = *reinterpret_cast<const uint2 *>(wbi + (int64_t)n * (kSpan / 64) + (kSpan / 128) * kh);
+  }
 
   const RbConsts kc = rb_consts();
   const uint32_t sh = 16u * (uint32_t)(kq >> 1);
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kSteps / 2; ++s) {
-    const uint32_t swd = s == 0 ? sw.x : sw.y, bwd = s == 0 ? bw.x : bw.y;
-    const uint32_t sc = rb_pack_scale_bias((swd >> sh) & 0xFFFFu, (bwd >> sh) & 0xFFFFu);
+  for (int p = 0; p < NT; ++p) {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(rb_h8, hv[s][q]),
-                                                   rb_rebuild(code[s][q], sc, kc), acc, 0, 0, 0);
+    for (int s = 0; s < kSteps / 2; ++s) {
+      const uint32_t swd = s == 0 ? sw[p].x : sw[p].y, bwd = s == 0 ? bw[p].x : bw[p].y;
+      const uint32_t sc = rb_pack_scale_bias((swd >> sh) & 0xFFFFu, (bwd >> sh) & 0xFFFFu);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(rb_h8, hv[s][q]),
+                                                     rb_rebuild(code[p][s][q], sc, kc), acc, 0, 0, 0);
+    }
+    // row 0 (first half) of columns 0-7 and row 1 (second half) of columns
+    // 8-15 sit in lanes 0-15 (kq = 0), elements 0 and 1
+    if (kq == 0) s_part[j][16 * p + c16] = live ? (c16 < 8 ? acc[0] : acc[1]) : 0.f;
   }
-  // row 0 (first half) of columns 0-7 and row 1 (second half) of columns
-  // 8-15 sit in lanes 0-15 (kq = 0), elements 0 and 1
-  if (kq == 0) s_part[j][c16] = live ? (c16 < 8 ? acc[0] : acc[1]) : 0.f;
   if (lane == 0 && !shared) s_gate[j] = g_slot;
   __syncthreads();
-  if (tid < 8) {
+  if (tid < 8 * NT) {
+    const int p = tid >> 3, c = 16 * p + (tid & 7);
     float y = 0.f;
-    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * (s_part[jj][tid] + s_part[jj][tid + 8]);
-    y += s_part[k][tid] + s_part[k][tid + 8];
-    a.y[(int64_t)t * d + 8 * cc + tid] = y;
+    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * (s_part[jj][c] + s_part[jj][c + 8]);
+    y += s_part[k][c] + s_part[k][c + 8];
+    a.y[(int64_t)t * d + 8 * NT * cc + tid] = y;
   }
 }
 
@@ -357,7 +391,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start
                          hipEvent_t dn_stop) {
   const int vpl = (a.E + 63) / 64;
   const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
-  const size_t xlds = (size_t)a.T * a.d * 2;  // the call's activations
+  // the call's activations, then each wave's partial sums (2 x 256 floats)
+  const size_t xlds = (size_t)a.T * a.d * 2 + (size_t)(a.d / kSpan) * 2 * 256 * sizeof(float);
   if (a.T == 1) {
     if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
     else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
@@ -373,8 +408,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 g2(a.T * (a.d / 8)), b2(64 * (a.k + 1));
-  hipExtLaunchKernelGGL(decode_dn_kernel, g2, b2, 0, s, nullptr, dn_stop, 0, a);
+  // Three down workgroups (k + 1 waves each) fit a CU, 768 on MI355X's 256
+  // CUs: calls that would need more take 16 output columns per workgroup, so
+  // every workgroup is resident at once
+  const dim3 b2(64 * (a.k + 1));
+  if ((int64_t)a.T * (a.d / 8) > kDnResident)
+    hipExtLaunchKernelGGL(decode_dn_kernel<2>, dim3(a.T * (a.d / 16)), b2, 0, s, nullptr, dn_stop, 0, a);
+  else
+    hipExtLaunchKernelGGL(decode_dn_kernel<1>, dim3(a.T * (a.d / 8)), b2, 0, s, nullptr, dn_stop, 0, a);
   return hipGetLastError();
 }
 
