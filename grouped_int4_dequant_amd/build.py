@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_int4.so")
-SOURCES = ["moe_api.hip", "routing_kernels.hip", "gemm_kernels.hip", "decode_kernels.hip", "router_kernels.hip"]
+SOURCES = ["moe_api.hip", "routing_kernels.hip", "gemm_kernels.hip", "gemm_kernels_small.hip", "decode_kernels.hip",
+           "router_kernels.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -61,6 +61,13 @@
 
 #include <type_traits>
 
+// The main build is launch_gemm (units of up to 96 rows, two workgroups per
+// CU); gemm_kernels_small.hip compiles this file again as launch_gemm_small
+// (units of up to 32 rows, three workgroups per CU).
+#ifndef MOE_GEMM_LAUNCH
+#define MOE_GEMM_LAUNCH launch_gemm
+#endif
+
 namespace moe {
 namespace {
 
@@ -600,13 +607,18 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
 template <int MODE, bool AF16, bool WX, bool CHECK, int CB, bool BUF, bool PREP>
 __device__ __forceinline__ void run_rows(const GemmProblem &P, const Unit &U, uint8_t *lds, const int *s_arow,
                                          uint32_t *tab) {
-  switch ((U.nr + 15) >> 4) {
-    case 1: run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
-    case 2: run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
-    case 3: run_unit<MODE, AF16, WX, CHECK, 3, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
-    case 4: run_unit<MODE, AF16, WX, CHECK, 4, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
-    case 5: run_unit<MODE, AF16, WX, CHECK, 5, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
-    default: run_unit<MODE, AF16, WX, CHECK, 6, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+  if constexpr (kUnitRows <= 32) {  // the small-unit build: one or two row blocks
+    if (U.nr <= 16) run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF, PREP>(P, U, lds, s_arow, tab);
+    else            run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF, PREP>(P, U, lds, s_arow, tab);
+  } else {
+    switch ((U.nr + 15) >> 4) {
+      case 1: run_unit<MODE, AF16, WX, CHECK, 1, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+      case 2: run_unit<MODE, AF16, WX, CHECK, 2, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+      case 3: run_unit<MODE, AF16, WX, CHECK, 3, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+      case 4: run_unit<MODE, AF16, WX, CHECK, 4, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+      case 5: run_unit<MODE, AF16, WX, CHECK, 5, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+      default: run_unit<MODE, AF16, WX, CHECK, 6, CB, BUF, PREP>(P, U, lds, s_arow, tab); break;
+    }
   }
 }
 
@@ -707,10 +719,24 @@ __global__ __launch_bounds__(kGemmThreads, MOE_GEMM_WGS_PER_CU) void gemm_kernel
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start,
-                       hipEvent_t stop, bool expanded) {
+hipError_t MOE_GEMM_LAUNCH(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start,
+                           hipEvent_t stop, bool expanded) {
   const dim3 grid(a.total_wg), block(kGemmThreads);
   if (a.total_wg == 0) return hipSuccess;
+#ifdef MOE_GEMM_SMALL_BUILD
+  // the small-unit build serves the layer's two projections over fp16
+  // activations only
+  if (expanded || !a_f16 || (mode != kSwiGLU && mode != kStoreH)) return hipErrorInvalidValue;
+  const bool check = a.prob[0].overflow != nullptr;
+  if (mode == kSwiGLU) {
+    if (check) hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false, true>), grid, block, 0, s, start, stop, 0, a);
+    else       hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, start, stop, 0, a);
+  } else {
+    if (check) hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false, true>), grid, block, 0, s, start, stop, 0, a);
+    else       hipExtLaunchKernelGGL((gemm_kernel<kStoreH, true, false>), grid, block, 0, s, start, stop, 0, a);
+  }
+  return hipGetLastError();
+#else
   if (expanded) {  // layer GEMMs over expanded weights (unfused ablation)
     switch (mode) {
       case kSwiGLU: hipExtLaunchKernelGGL((gemm_kernel<kSwiGLU, true, true>), grid, block, 0, s, start, stop, 0, a); break;
@@ -742,8 +768,10 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, h
     hipExtLaunchKernelGGL((gemm_kernel<kStoreC, false, false>), grid, block, 0, s, start, stop, 0, a);
   }
   return hipGetLastError();
+#endif
 }
 
+#ifndef MOE_GEMM_SMALL_BUILD
 // Weights of `rows` rows of K inputs (all experts of a projection, stored
 // back to back) rebuilt once into fp16 in device memory, each 8-run in the
 // rebuild order, with the same arithmetic as the GEMM's on-chip rebuild.
@@ -839,5 +867,7 @@ hipError_t launch_expand(const uint32_t *q, const uint16_t *sc, const uint16_t *
   hipLaunchKernelGGL(expand_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, s, q, sc, bi, words, K, out);
   return hipGetLastError();
 }
+
+#endif  // MOE_GEMM_SMALL_BUILD
 
 }  // namespace moe

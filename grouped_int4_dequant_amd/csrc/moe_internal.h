@@ -12,7 +12,13 @@
 namespace moe {
 
 constexpr int kGroup = 64;         // weights per scale/bias group
-constexpr int kUnitRows = 96;      // max rows of one GEMM work unit (three 32-row blocks)
+// Max rows of one GEMM work unit: three 32-row blocks, or (the small-unit
+// GEMM build, for calls whose experts hold few rows each) one.
+#ifndef MOE_UNIT_ROWS
+#define MOE_UNIT_ROWS 96
+#endif
+constexpr int kUnitRows = MOE_UNIT_ROWS;
+constexpr int kUnitRowsSmall = 32;
 constexpr int kSubChunk = 64;      // tokens per routing bitmask (one wave's lanes)
 constexpr int kThreads = 256;      // threads per workgroup of the routing and combine kernels
 // Grouped-GEMM workgroup shape (compile-time; the defaults are the measured
@@ -152,6 +158,11 @@ struct GemmArgs {
 // kSwiGLU and kStoreH).
 hipError_t launch_gemm(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr, bool expanded = false);
+// The same GEMM compiled for units of at most kUnitRowsSmall rows (148
+// registers, three workgroups per CU): the layer's projections when its
+// experts hold about 20 rows or fewer on average.
+hipError_t launch_gemm_small(const GemmArgs &a, int mode, bool a_f16, hipStream_t s, hipEvent_t start = nullptr,
+                             hipEvent_t stop = nullptr, bool expanded = false);
 // Prepared copy of one projection's weights for E experts (prep_layout.h):
 // swiglu: rows 0..N/2-1 gate, N/2..N-1 up.
 hipError_t launch_prepare(const uint32_t *q, const uint16_t *sc, const uint16_t *bi, int E, int N, int K,

@@ -439,9 +439,13 @@ def test_ablation_full_config(moe, variant):
     layer, x, lg = upload(p, moe)
     routing = moe.alloc_routing(p.T, p.shape.E, p.shape.k)
     y = moe.layer_forward_ablation(layer, x, lg, variant, routing=routing)
+    # the default form at T=512 runs the small-unit GEMM build (32-row units);
+    # every ablation form runs the 96-row build: equal bit for bit
+    y_def = moe.layer_forward(layer, x, lg)
     torch.cuda.synchronize()
     check_routing(routing, O.route(p.logits, p.shape.k), p.T, p.shape.k)
     check_output(y.cpu().numpy(), O.moe_forward(p.layer, p.x, p.logits, p.shape.k), f"{variant} config 1")
+    assert np.array_equal(y.cpu().numpy(), y_def.cpu().numpy()), f"{variant} differs from the default form"
 
 
 def test_zero_tokens_is_a_noop(moe):
