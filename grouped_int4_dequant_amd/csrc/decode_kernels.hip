@@ -105,12 +105,16 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
 
   // ---- routing, repeated by every workgroup of a routed expert
   if (!shared && ONE) {
-    // one token: its k picks are the distinct experts, in slot order
+    // one token: its k picks are the distinct experts, in slot order. The
+    // workgroups of slot u stop after u + 1 rounds (the lower slots' weight
+    // requests go out sooner, so the last slot's stream meets less traffic);
+    // workgroup 0 runs all k, since it writes the ids and gates
     if (wave == 0) {
       int id;
       float g;
-      topk_wave<VPL>(a.logits, E, k, lane, id, g);
-      if (lane < k) {
+      const int rounds = blockIdx.x == 0 ? k : min(u + 1, k);
+      topk_wave<VPL>(a.logits, E, rounds, lane, id, g);
+      if (lane < rounds) {
         s_ids[lane] = id;
         s_uexp[lane] = id;
         s_umask[lane] = 1u;
