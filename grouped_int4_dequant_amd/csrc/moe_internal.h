@@ -64,6 +64,7 @@ struct TopkArgs {
   uint16_t *x16;            // fp16 [T][d], each 8-element run stored as 0,4,1,5,2,6,3,7
   int d;
   uint32_t *overflow;       // nullable: MOE_OVERFLOW_X when an x16 value is not finite
+  int topk_wgs;             // set by launch_topk: workgroups [0, topk_wgs) route, the rest convert x
 };
 
 // y[t] = sum_j w[t][j] * o[pair_pos[t*k+j]] + o_sh[t], slot order, fp32.

@@ -7,7 +7,8 @@
 // la GPU"). Here that is two kernels on one stream (three above 32768
 // pairs) whose grids depend only on T, never on routed counts:
 //
-//   topk  one wave per token. Every candidate becomes a 64-bit key
+//   topk  one wave per token (the x -> fp16 conversion in workgroups of its
+//         own, after the routing ones). Every candidate becomes a 64-bit key
 //         (order-preserving logit bits, then the inverted expert index), so
 //         "larger logit, then lower index" is plain unsigned order and all
 //         keys are distinct. Each lane sorts its own keys; k rounds of a wave
@@ -74,15 +75,21 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t two_bf16) {
 template <int VPL, bool CHECK>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x % kWave;
-  const int gwave = blockIdx.x * kWaves + threadIdx.x / kWave;
-  const int nwaves = gridDim.x * kWaves;
-  // x (bf16, natural order) -> x16 (fp16, each 8-run stored as 0,4,1,5,2,6,3,7).
-  // The first kUnroll 16-byte chunks of this thread are requested before the
-  // top-k, so their latency hides behind it.
+  if ((int)blockIdx.x < a.topk_wgs) {
+    // routing workgroups: one token per wave
+    const int gwave = blockIdx.x * kWaves + threadIdx.x / kWave;
+    const int nwaves = a.topk_wgs * kWaves;
+    for (int t = gwave; t < a.T; t += nwaves) route_token<VPL>(a, t, lane);
+    return;
+  }
+  // conversion workgroups (their own, so a routing workgroup ends with its
+  // last top-k): x (bf16, natural order) -> x16 (fp16, each 8-run stored as
+  // 0,4,1,5,2,6,3,7), kUnroll 16-byte chunks per thread in flight
   constexpr int kUnroll = 4;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int cb = blockIdx.x - a.topk_wgs, ncb = gridDim.x - a.topk_wgs;
+  const int64_t stride = (int64_t)ncb * kThreads;
   const int64_t n8 = a.x16 ? (int64_t)a.T * a.d / 8 : 0;
-  int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t i0 = (int64_t)cb * kThreads + threadIdx.x;
   uint4 v[kUnroll];
   auto load = [&]() {
 #pragma unroll
@@ -92,7 +99,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
   };
   load();
-  for (int t = gwave; t < a.T; t += nwaves) route_token<VPL>(a, t, lane);
   for (; i0 < n8; i0 += kUnroll * stride) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -475,12 +481,13 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_topk(const TopkArgs &args, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  TopkArgs a = args;
   const int vpl = (a.E + kWave - 1) / kWave;
-  int nwg = (int)ceil_div(a.T, kWaves);
-  if (a.x16) nwg = (int)std::max<int64_t>(nwg, std::min<int64_t>(1024, ceil_div((int64_t)a.T * a.d / 8, 4 * kThreads)));
-  nwg = std::min(nwg, 4096);
-  const dim3 grid(nwg), block(kThreads);
+  // routing workgroups (one token per wave), then conversion workgroups
+  a.topk_wgs = (int)std::min<int64_t>(std::max<int64_t>(ceil_div(a.T, kWaves), 1), 4096);
+  const int conv = a.x16 ? (int)std::min<int64_t>(1024, ceil_div((int64_t)a.T * a.d / 8, 4 * kThreads)) : 0;
+  const dim3 grid(a.topk_wgs + conv), block(kThreads);
   if (a.overflow) {
     if (vpl <= 1)       hipExtLaunchKernelGGL((topk_kernel<1, true>), grid, block, 0, s, start, stop, 0, a);
     else if (vpl <= 2)  hipExtLaunchKernelGGL((topk_kernel<2, true>), grid, block, 0, s, start, stop, 0, a);
