@@ -46,6 +46,12 @@ constexpr int kSpan = 512;          // inputs per wave
 constexpr int kSteps = kSpan / 128;  // 128-input steps per wave
 constexpr int kMaxWaves = 8;         // gate/up waves per workgroup (d <= 4096)
 constexpr int kDnResident = 768;      // down workgroups resident at once (3 per CU)
+// Calls of up to this many tokens run one gate/up item per (token, slot) pair;
+// longer ones one item per distinct expert.
+#ifndef MOE_DECODE_PAIR_MAXT
+#define MOE_DECODE_PAIR_MAXT 8
+#endif
+constexpr int kDecodePairMaxT = MOE_DECODE_PAIR_MAXT;
 
 // Position of the r-th set bit of m (r < popcount(m)).
 __device__ __forceinline__ int nth_bit(uint32_t m, int r) {
@@ -76,7 +82,9 @@ __device__ __forceinline__ uint4 x_chunk_h8(uint4 v) {
 // Several tokens with up to 512 experts: five waves per SIMD (every T = 4
 // workgroup resident at once); the one-token and 1024-expert forms keep
 // their registers.
-template <int VPL, bool ONE>
+// PAIR (several tokens): each routed item is one (token, slot) pair, as at
+// T = 1, instead of one distinct expert for all the tokens that picked it.
+template <int VPL, bool ONE, bool PAIR>
 __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void decode_gu_kernel(DecodeArgs a) {
   __shared__ int s_ids[kDecodeMaxPairs];
   __shared__ uint32_t s_bits[MOE_MAX_EXPERTS / 32];
@@ -92,6 +100,11 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
   const int chunks = a.fmax / 16;
   const int u = blockIdx.x / chunks, hc = blockIdx.x - u * chunks;
   const bool shared = u == P;
+  // pair items: token pt, slot pj (one token: item u is slot u)
+  constexpr bool kPairs = ONE || PAIR;
+  const int pt = kPairs && !shared ? u / k : 0, pj = kPairs && !shared ? u - pt * k : 0;
+  // one token's activations, requested at the start (one token, or a pair)
+  const bool x_one = ONE || (PAIR && !shared);
 
   // ---- the call's activations (bf16 [T][d]) go to LDS. One token: each
   // thread's chunk is requested first, so its latency hides behind the
@@ -101,29 +114,25 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
   extern __shared__ uint4 s_x[];  // [T * d / 8]
   float(*s_red)[2][256] = reinterpret_cast<float(*)[2][256]>(s_x + T * (a.d / 8));  // [waves][2][256]
   uint4 xr0 = make_uint4(0u, 0u, 0u, 0u);
-  if (ONE) xr0 = reinterpret_cast<const uint4 *>(a.x)[tid];
+  if (x_one) xr0 = reinterpret_cast<const uint4 *>(a.x)[pt * nthreads + tid];  // nthreads = d / 8
 
   // ---- routing, repeated by every workgroup of a routed expert
-  if (!shared && ONE) {
-    // one token: its k picks are the distinct experts, in slot order. The
-    // workgroups of slot u stop after u + 1 rounds (the lower slots' weight
-    // requests go out sooner, so the last slot's stream meets less traffic);
-    // workgroup 0 runs all k, since it writes the ids and gates
+  if (!shared && kPairs) {
+    // pair (token pt, slot pj): only token pt's top-k, and only its first
+    // pj + 1 rounds (the lower slots' weight requests go out sooner, so the
+    // last slots' streams meet less traffic); the first workgroup of slot 0
+    // runs all k, since it writes the token's ids and gates
     if (wave == 0) {
       int id;
       float g;
-      const int rounds = blockIdx.x == 0 ? k : min(u + 1, k);
-      topk_wave<VPL>(a.logits, E, rounds, lane, id, g);
-      if (lane < rounds) {
-        s_ids[lane] = id;
-        s_uexp[lane] = id;
-        s_umask[lane] = 1u;
-        if (blockIdx.x == 0) {
-          a.ids[lane] = id;
-          a.gates[lane] = g;
-        }
+      const bool writer = pj == 0 && hc == 0;
+      const int rounds = writer ? k : min(pj + 1, k);
+      topk_wave<VPL>(a.logits + (int64_t)pt * E, E, rounds, lane, id, g);
+      if (lane == pj) s_uexp[0] = id;
+      if (writer && lane < k) {
+        a.ids[pt * k + lane] = id;
+        a.gates[pt * k + lane] = g;
       }
-      if (lane == 0) s_U = k;
     }
     __syncthreads();
   } else if (!shared) {
@@ -170,6 +179,10 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
     if (a.f_sh == 0) return;
     fe = a.f_sh;
     mask = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
+  } else if (kPairs) {
+    e = s_uexp[0];
+    mask = 1u << pt;
+    fe = a.f;
   } else {
     if (u >= s_U) return;
     e = s_uexp[u];
@@ -200,10 +213,10 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
   // activations into LDS as fp16 in the rebuild order (their loads were
   // issued first), converted once per workgroup; then row c16's fragments:
   // a token of the mask, else the first one again (a row never read)
-  if (ONE) {
+  if (x_one) {
     const uint4 xc = x_chunk_h8(xr0);
-    s_x[tid] = xc;
-    if (blockIdx.x == 0)
+    s_x[pt * nthreads + tid] = xc;
+    if (pj == 0 && hc == 0 && !shared)  // each token's x checked once
       note_overflow(a.overflow, f16x2_nonfinite(xc.x) || f16x2_nonfinite(xc.y) || f16x2_nonfinite(xc.z) ||
                                     f16x2_nonfinite(xc.w), MOE_OVERFLOW_X);
   } else {
@@ -288,8 +301,8 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
           up += s_red[w][1][4 * lane + i];
         }
         const int t = nth_bit(mask, r);
-        // one token: distinct expert u is slot u
-        const int slot = shared ? k : ONE ? u : s_uslot[u][t];
+        // pairs: the item's slot
+        const int slot = shared ? k : kPairs ? pj : s_uslot[u][t];
         // fp16, each 8 columns in the rebuild order, as the down MFMAs take it
         const int n = 16 * hc + c16;
         const float hv = g / (1.f + __expf(-g)) * up;
@@ -391,25 +404,25 @@ bool decode_supported(int T, const moe_layer_t *L) {
          L->E <= MOE_MAX_EXPERTS;
 }
 
+template <bool ONE, bool PAIR>
+static void launch_decode_gu(const DecodeArgs &a, int vpl, dim3 g, dim3 b, size_t lds, hipStream_t s, hipEvent_t start,
+                             hipEvent_t stop) {
+  if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, ONE, PAIR>), g, b, lds, s, start, stop, 0, a);
+  else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, ONE, PAIR>), g, b, lds, s, start, stop, 0, a);
+  else if (vpl <= 4)  hipExtLaunchKernelGGL((decode_gu_kernel<4, ONE, PAIR>), g, b, lds, s, start, stop, 0, a);
+  else if (vpl <= 8)  hipExtLaunchKernelGGL((decode_gu_kernel<8, ONE, PAIR>), g, b, lds, s, start, stop, 0, a);
+  else                hipExtLaunchKernelGGL((decode_gu_kernel<16, ONE, PAIR>), g, b, lds, s, start, stop, 0, a);
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start, hipEvent_t gu_stop,
                          hipEvent_t dn_stop) {
   const int vpl = (a.E + 63) / 64;
   const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
   // the call's activations, then each wave's partial sums (2 x 256 floats)
   const size_t xlds = (size_t)a.T * a.d * 2 + (size_t)(a.d / kSpan) * 2 * 256 * sizeof(float);
-  if (a.T == 1) {
-    if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 4)  hipExtLaunchKernelGGL((decode_gu_kernel<4, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 8)  hipExtLaunchKernelGGL((decode_gu_kernel<8, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else                hipExtLaunchKernelGGL((decode_gu_kernel<16, true>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-  } else {
-    if (vpl <= 1)       hipExtLaunchKernelGGL((decode_gu_kernel<1, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 2)  hipExtLaunchKernelGGL((decode_gu_kernel<2, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 4)  hipExtLaunchKernelGGL((decode_gu_kernel<4, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else if (vpl <= 8)  hipExtLaunchKernelGGL((decode_gu_kernel<8, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-    else                hipExtLaunchKernelGGL((decode_gu_kernel<16, false>), g1, b1, xlds, s, gu_start, gu_stop, 0, a);
-  }
+  if (a.T == 1)                     launch_decode_gu<true, false>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
+  else if (a.T <= kDecodePairMaxT)  launch_decode_gu<false, true>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
+  else                              launch_decode_gu<false, false>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // Three down workgroups (k + 1 waves each) fit a CU, 768 on MI355X's 256
