@@ -42,9 +42,9 @@ TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip",
                    "grouped_int4_dequant_amd/csrc/routing_kernels.hip")
-TRAFFIC_DIGEST = "e0e50e41df3f32f6bb9100e00d7e3600faa4abcfebecaaa791ce0d66612e20d6"
-TRAFFIC_BYTES = {"gate_up": (185642.9 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85494.0 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.7) * 1024}
+TRAFFIC_DIGEST = "83bb9f23abd0f184f812d8c188901e7f06fe1253cb070a7a45fbb357511ac615"
+TRAFFIC_BYTES = {"gate_up": (185593.4 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85495.4 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
 
 
 def sources_digest():
