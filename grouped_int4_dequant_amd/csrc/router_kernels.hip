@@ -27,6 +27,7 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRouterRows = 32;     // tokens per workgroup
 constexpr int kRouterExperts = 64;  // experts per workgroup (16 per wave)
@@ -63,21 +64,20 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     const int u = tid + 256 * i, r = u >> 5, j = u & 31;
     return reinterpret_cast<uint4 *>(&s_x[buf][r * kRowBytes + 16 * (j ^ (r & 15))]);
   };
-  uint4 x0, x1, x2, x3;  // this thread's four units of the next chunk
+  // this thread's four units of the next chunk (compiler vector type: a
+  // select of the struct form costs about 40 more registers)
+  u4 xr[4];
   auto live = [&](int c, int i) { return c * kChunkSteps * 32 + 8 * ((tid + 256 * i) & 31) < a.d; };
   auto load_x = [&](int c) {
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 v0 = *x_src(c, 0), v1 = *x_src(c, 1), v2 = *x_src(c, 2), v3 = *x_src(c, 3);
-    x0 = live(c, 0) ? v0 : z;
-    x1 = live(c, 1) ? v1 : z;
-    x2 = live(c, 2) ? v2 : z;
-    x3 = live(c, 3) ? v3 : z;
+    u4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u4 *>(x_src(c, i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = live(c, i) ? v[i] : u4{0u, 0u, 0u, 0u};
   };
   auto store_x = [&](int buf) {
-    *x_dst(buf, 0) = x0;
-    *x_dst(buf, 1) = x1;
-    *x_dst(buf, 2) = x2;
-    *x_dst(buf, 3) = x3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u4 *>(x_dst(buf, i)) = xr[i];
   };
   typedef uint4 WChunk[kChunkSteps];
   auto load_w = [&](WChunk &cw, int c) {
@@ -98,10 +98,10 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int u = 0; u < kChunkSteps; ++u) {
       const int j = 4 * u + kq;
-      const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
-      const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
       const bf8 wv = __builtin_bit_cast(bf8, w[u]);
+      const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), wv, acc0, 0, 0, 0);
+      const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), wv, acc1, 0, 0, 0);
     }
     store_x((c + 1) & 1);
