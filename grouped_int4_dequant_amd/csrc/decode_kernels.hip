@@ -296,9 +296,23 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
       const int r = 4 * kq + i;  // row of the MFMA tile = r-th token of the mask
       if (r < nrows) {
         float g = 0.f, up = 0.f;
-        for (int w = 0; w < nwaves; ++w) {
-          g += s_red[w][0][4 * lane + i];
-          up += s_red[w][1][4 * lane + i];
+        if (nwaves == 4) {  // d = 2048: every partial requested before the first add
+          float gv[4], uv[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            gv[w] = s_red[w][0][4 * lane + i];
+            uv[w] = s_red[w][1][4 * lane + i];
+          }
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            g += gv[w];
+            up += uv[w];
+          }
+        } else {
+          for (int w = 0; w < nwaves; ++w) {
+            g += s_red[w][0][4 * lane + i];
+            up += s_red[w][1][4 * lane + i];
+          }
         }
         const int t = nth_bit(mask, r);
         // pairs: the item's slot
@@ -390,8 +404,22 @@ __global__ __launch_bounds__(64 * kDecodeMaxSlots) void decode_dn_kernel(DecodeA
   if (tid < 8 * NT) {
     const int p = tid >> 3, c = 16 * p + (tid & 7);
     float y = 0.f;
-    for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * (s_part[jj][c] + s_part[jj][c + 8]);
-    y += s_part[k][c] + s_part[k][c + 8];
+    if (k == 8) {  // top-8: every partial and gate requested before the first add
+      float gv[8], pa[9], pb[9];
+#pragma unroll
+      for (int jj = 0; jj < 9; ++jj) {
+        pa[jj] = s_part[jj][c];
+        pb[jj] = s_part[jj][c + 8];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) gv[jj] = s_gate[jj];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) y += gv[jj] * (pa[jj] + pb[jj]);
+      y += pa[8] + pb[8];
+    } else {
+      for (int jj = 0; jj < k; ++jj) y += s_gate[jj] * (s_part[jj][c] + s_part[jj][c + 8]);
+      y += s_part[k][c] + s_part[k][c + 8];
+    }
     a.y[(int64_t)t * d + 8 * NT * cc + tid] = y;
   }
 }
