@@ -375,9 +375,10 @@ int moe_layer_forward_checked(const moe_layer_t *L, const uint16_t *x, const flo
  * kernels, events[3] at the end of the gate/up kernel and events[4] at the end
  * of the last kernel (down + combine). In the few-token form without routing
  * outputs there are no routing kernels: events[0] and events[1] are recorded
- * as markers and events[2] is the start of the gate/up kernel. events: 5
- * caller-created hipEvent_t handles (host array). Requires T >= 1; otherwise
- * as moe_layer_forward.
+ * as markers and events[2] is the start of the gate/up kernel. events: host
+ * array of 5 caller-created hipEvent_t handles; a null entry leaves that
+ * point unrecorded (fewer events, less timing overhead). Requires T >= 1;
+ * otherwise as moe_layer_forward.
  */
 int moe_layer_forward_timed(const moe_layer_t *L, const uint16_t *x, const float *logits,
                             int32_t T, float *y, const moe_routing_t *routing,
