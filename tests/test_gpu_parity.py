@@ -286,6 +286,39 @@ def test_layer_bit_reproducible(moe, index):
         assert diff == 0, f"repeat {r}: {diff} output elements differ"
 
 
+@pytest.mark.parametrize("keep", [(0, 1, 2, 3, 4), (2, 3), ()], ids=["all", "gate_up", "none"])
+@pytest.mark.parametrize("index", [0, 1])
+def test_layer_forward_timed_matches_plain(moe, index, keep):
+    """moe_layer_forward_timed computes what moe_layer_forward computes, bit
+    for bit, with all five events, with only the gate/up pair (the
+    benchmark's timed calls) or with every entry null; each recorded pair
+    spans a positive time."""
+    import ctypes
+    import bench
+    from grouped_int4_dequant_amd import binding as B
+    p = S.make_problem(index)
+    say(f"timed forward config {index} T={p.T} events {keep}")
+    layer, x, lg = upload(p, moe)
+    ws = moe.alloc_workspace(moe.workspace_bytes(p.T, layer))
+    ref = moe.layer_forward(layer, x, lg, ws=ws).clone()
+    lib = B.load()
+    lib.moe_layer_forward_timed.argtypes = [ctypes.POINTER(B.MoeLayerT), B._P, B._P, B._I32, B._P, B._P, B._P,
+                                            ctypes.c_size_t, B._P, ctypes.POINTER(B._P)]
+    lib.moe_layer_forward_timed.restype = ctypes.c_int
+    hip = bench.hip_runtime()
+    evs = [bench.HipEvent(hip) for _ in range(5)]
+    arr = (B._P * 5)(*[evs[i].handle if i in keep else None for i in range(5)])
+    y = torch.empty_like(ref)
+    st = lib.moe_layer_forward_timed(ctypes.byref(layer.c), x.data_ptr(), lg.data_ptr(), p.T, y.data_ptr(), None,
+                                     ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream, arr)
+    assert st == 0, moe.status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+    for i in range(4):
+        if i in keep and i + 1 in keep:
+            assert evs[i].elapsed_time(evs[i + 1]) > 0.0, (i, keep)
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_config4(moe, T):
     """Config 4's parity schedule: routing checked on every one of the 1000
