@@ -45,8 +45,8 @@ TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip",
                    "grouped_int4_dequant_amd/csrc/routing_kernels.hip")
 TRAFFIC_DIGEST = "9713ee73fbf316c526107a2abc25929925cb8a385ea2b939e6aa3fcd2a10db83"
-TRAFFIC_BYTES = {"gate_up": (185593.4 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85495.4 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
+TRAFFIC_BYTES = {"gate_up": (185649.7 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85494.3 * 2.0 + 73728.0 + 37144.5 * 2.0 + 16384.5) * 1024}
 
 
 def sources_digest():
