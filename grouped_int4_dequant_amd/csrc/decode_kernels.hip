@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
         const int slot = shared ? k : kPairs ? pj : s_uslot[u][t];
         // fp16, each 8 columns in the rebuild order, as the down MFMAs take it
         const int n = 16 * hc + c16;
-        const float hv = g / (1.f + __expf(-g)) * up;
+        const float hv = swiglu(g, up);
         note_overflow(a.overflow, f16_out_of_range(hv), MOE_OVERFLOW_H);
         a.h[((int64_t)t * (k + 1) + slot) * a.fmax + (n & ~7) + 2 * (n & 3) + ((n >> 2) & 1)] =
             __builtin_bit_cast(uint16_t, (_Float16)hv);

@@ -513,7 +513,7 @@ __device__ __forceinline__ void run_unit(const GemmProblem &P, const Unit &U, ui
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * rb + 4 * kq + i;
             const float g = acc[rb][cb][i], u = acc[rb][cb + kHalf][i];
-            const float h = g / (1.f + __expf(-g)) * u;
+            const float h = swiglu(g, u);
             if (CHECK) bad |= r < nr && f16_out_of_range(h);
             *reinterpret_cast<uint16_t *>(lds + r * 256 + 16 * ((lc >> 3) ^ (r & 15)) + 2 * (lc & 7)) =
                 f32_to_f16_bits(h);

@@ -53,6 +53,15 @@ __device__ __forceinline__ void note_overflow(uint32_t *flag, bool bad, uint32_t
 }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// SwiGLU of one (gate, up) pair: silu(g) * u with silu(g) = g / (1 + e^-g).
+// The reciprocal is one v_rcp_f32 (about 1 ulp) instead of a correctly
+// rounded division (about ten instructions per element, a fifth of the
+// gate/up kernel's VALU work at 64 rows per expert); h is stored in fp16,
+// whose rounding is 2^13 times coarser.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 // ------------------------------------------------------------------ routing
 struct TopkArgs {
   const float *logits;
