@@ -44,9 +44,9 @@ TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_internal.h",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip",
                    "grouped_int4_dequant_amd/csrc/routing_kernels.hip")
-TRAFFIC_DIGEST = "9713ee73fbf316c526107a2abc25929925cb8a385ea2b939e6aa3fcd2a10db83"
-TRAFFIC_BYTES = {"gate_up": (185649.7 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85494.3 * 2.0 + 73728.0 + 37144.5 * 2.0 + 16384.5) * 1024}
+TRAFFIC_DIGEST = "389c4e4978e6004c69bd646b994739ed807e437ad8734d9d58c1f13ffc8dcd6c"
+TRAFFIC_BYTES = {"gate_up": (185244.2 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85497.6 * 2.0 + 73728.0 + 37144.6 * 2.0 + 16384.6) * 1024}
 
 
 def sources_digest():
