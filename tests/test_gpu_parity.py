@@ -366,6 +366,18 @@ def test_decode_shapes(moe, T, E, k, f_sh, with_routing):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"decode T={T} E={E} k={k}")
 
 
+@pytest.mark.parametrize("T,d,E,k", [(1, 1024, 256, 8), (4, 1024, 64, 8), (1, 4096, 128, 4), (3, 4096, 256, 8)])
+def test_decode_other_widths(moe, T, d, E, k):
+    """Decode at d = 1024 and 4096 (two and eight gate/up waves, so the
+    partial sums take the general reduction loop; k = 4 also in the down
+    kernel's combine)."""
+    p = S.make_custom(T, S.LayerShape(d=d, f=512, E=E, k=k, f_sh=512), seed=200 + T + d + E + k)
+    say(f"decode T={T} d={d} E={E} k={k}")
+    y, routing = run_layer(moe, p, with_routing=True)
+    check_routing(routing, O.route(p.logits, k), T, k)
+    check_output(y, O.moe_forward(p.layer, p.x, p.logits, k), f"decode T={T} d={d} E={E} k={k}")
+
+
 @pytest.mark.parametrize("T,zero_row", [(4, 1), (1, None), (1, 0)])
 def test_decode_tied_logits(moe, T, zero_row):
     """Exact ties (and -0.0 against +0.0) decide which experts the decode
