@@ -281,6 +281,7 @@ def main():
     }
 
     out["router"] = bench_router(moe, S, torch, x, sh, args.steps)
+    out["router_t1"] = bench_router_graph(moe, S, torch, x[:1].contiguous(), sh)
     if args.decode_steps > 0:
         out["decode_t1"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events)
         out["decode_t4"] = bench_decode(moe, lib, B, S, torch, dev, stream, args.decode_steps, make_events, T=4)
@@ -318,6 +319,37 @@ def bench_router(moe, S, torch, x, sh, steps):
     us = e0.elapsed_time(e1) * 1e3 / steps
     return {"T": T, "d": sh.d, "E": sh.E, "us_per_call": us,
             "tflops": 2.0 * T * sh.d * sh.E / (us * 1e-6) / 1e12}
+
+
+def bench_router_graph(moe, S, torch, x, sh, n=200, reps=3):
+    """The router projection for a decode step's token (T = 1): n calls
+    captured in a HIP graph and replayed, so the GPU time per call is the
+    device's and not the host's call rate."""
+    T = x.shape[0]
+    w = S.draw_router(sh.E, sh.d, np.random.default_rng(1234))
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(x.device)
+    lg = torch.empty((T, sh.E), dtype=torch.float32, device=x.device)
+    for _ in range(5):
+        moe.router_logits(x, wt, logits=lg)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                moe.router_logits(x, wt, logits=lg)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+    return {"T": T, "d": sh.d, "E": sh.E, "us_per_call": us, "weight_gbps": sh.E * sh.d * 2 / (us * 1e-6) / 1e9}
 
 
 def bench_prefill_configs(moe, S, torch, dev, steps):

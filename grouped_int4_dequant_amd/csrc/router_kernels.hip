@@ -14,7 +14,9 @@
 // chunk loop body has no per-step branch (columns past d are staged as
 // zeros, which add exactly zero to accumulators that start at +0, and the
 // chunk count is rounded up to the unroll of two), so the compiler keeps the
-// next chunk's loads in flight across iterations.
+// next chunk's loads in flight across iterations. Calls of at most 16 tokens
+// take a second form (router_small_kernel below) that spreads W_r over four
+// times as many workgroups.
 
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -125,10 +127,69 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
+// Few tokens (T <= 16, the decode shape): one 16-row MFMA block holds every
+// token, so a workgroup takes 16 experts and splits the inputs over its eight
+// waves, each requesting its x and W_r operands eight steps at a time before
+// the first MFMA. W_r is then streamed by E / 16 workgroups instead of the
+// E / 64 of the block form, whose four-wave workgroups each pull 256 KiB
+// through one CU. The waves' partial sums meet in LDS and are added in wave
+// order, so repeated calls give identical logits.
+constexpr int kSmallRows = 16;   // tokens of the one row block
+constexpr int kSmallWaves = 8;   // input slices per workgroup
+constexpr int kSmallBatch = 8;   // 32-input steps requested at once
+__global__ __launch_bounds__(64 * kSmallWaves) void router_small_kernel(RouterArgs a) {
+  __shared__ f4 s_part[kSmallWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, kq = lane >> 4;
+  const int e = blockIdx.x * 16 + c16;
+  // experts past the end read the last valid one, token rows past T the
+  // last token (neither is stored)
+  const int ec = min(e, a.E - 1), tr = min(c16, a.T - 1);
+  const int steps = a.d / 32;
+  const int s0 = wave * steps / kSmallWaves, s1 = (wave + 1) * steps / kSmallWaves;
+  // lane (c16, kq): A row c16 (a token) and B column c16 (an expert), inputs
+  // 32 s + 8 kq .. + 7 of step s
+  const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (int64_t)tr * a.d) + kq;
+  const uint4 *wr = reinterpret_cast<const uint4 *>(a.w + (int64_t)ec * a.d) + kq;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  for (int sb = s0; sb < s1; sb += kSmallBatch) {
+    uint4 xv[kSmallBatch], wv[kSmallBatch];
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u) {
+      const int st = min(sb + u, s1 - 1);
+      xv[u] = xr[4 * st];
+      wv[u] = wr[4 * st];
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u)
+      if (sb + u < s1)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xv[u]), __builtin_bit_cast(bf8, wv[u]),
+                                                      acc, 0, 0, 0);
+  }
+  s_part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f4 sum = s_part[0][lane];
+#pragma unroll
+  for (int w = 1; w < kSmallWaves; ++w) sum += s_part[w][lane];
+  // element i of lane (c16, kq): token 4 kq + i, expert c16
+  if (e < a.E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * kq + i;
+      if (t < a.T) a.logits[(int64_t)t * a.E + e] = sum[i];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.T <= kSmallRows) {
+    hipLaunchKernelGGL(router_small_kernel, dim3((unsigned)ceil_div(a.E, 16)), dim3(64 * kSmallWaves), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)ceil_div(a.T, kRouterRows), (unsigned)ceil_div(a.E, kRouterExperts));
   hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -401,7 +401,8 @@ def _router_bound(x_bits, w_bits):
     return (d - 1) * 2.0 ** -24 * (np.abs(O.bf16_value(x_bits)) @ np.abs(O.bf16_value(w_bits)).T)
 
 
-@pytest.mark.parametrize("T,d,E", [(2048, 2048, 256), (37, 96, 20), (1, 32, 1), (130, 512, 1024), (45, 2080, 70)])
+@pytest.mark.parametrize("T,d,E", [(2048, 2048, 256), (37, 96, 20), (1, 32, 1), (130, 512, 1024), (45, 2080, 70),
+                                   (1, 2048, 256), (16, 2048, 256), (17, 2048, 256), (9, 96, 20), (3, 2080, 1000)])
 def test_router_logits_match_oracle(moe, T, d, E):
     say(f"router T={T} d={d} E={E}")
     x, w = S.make_router_problem(T, d, E, seed=T + d + E)
@@ -503,7 +504,8 @@ def test_zero_tokens_is_a_noop(moe):
 
 # ------------------------------------------------------ router fused with top-k
 @pytest.mark.parametrize("T,d,E,k", [(2048, 2048, 256, 8), (37, 96, 20, 3), (1, 64, 256, 8), (130, 512, 128, 8),
-                                     (64, 256, 16, 16), (70, 512, 300, 8), (45, 2080, 70, 4)])
+                                     (64, 256, 16, 16), (70, 512, 300, 8), (45, 2080, 70, 4),
+                                     (16, 2048, 256, 8), (5, 2080, 1000, 13)])
 def test_router_topk_matches_own_logits(moe, T, d, E, k):
     """moe_router_topk: its logits equal moe_router_logits' bit for bit, its
     picks equal the oracle's top-k of those same fp32 logits bit for bit, its
