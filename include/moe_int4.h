@@ -215,7 +215,11 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E);
  * sum_k x[t][k] * w_r[e][k]. x bf16 [T][d] and w_r bf16 [E][d] (device, row
  * major, 16-byte aligned, caller-owned); logits fp32 [T][E] (device, written).
  * Products are exact in fp32 and accumulate in fp32 in a fixed order, so a
- * call is deterministic. Errors: MOE_EINVAL (null or unaligned pointer,
+ * call is deterministic. Calls of up to 16 tokens use a second kernel form
+ * (16 experts per workgroup, inputs split over eight waves) whose order
+ * differs, so a token's logits may differ in the last bits between a call of
+ * at most 16 tokens and a longer one; each is within the fp32 summation
+ * bound of the exact value. Errors: MOE_EINVAL (null or unaligned pointer,
  * T < 0, d < 1, E < 1), MOE_EUNSUPPORTED (d not a multiple of 32, E >
  * MOE_MAX_EXPERTS, T > MOE_MAX_CALL_TOKENS). T == 0 enqueues nothing. One
  * kernel; allocates nothing.
