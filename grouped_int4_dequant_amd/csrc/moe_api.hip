@@ -166,6 +166,7 @@ struct Workspace {
   uint16_t *x16, *h, *h_sh, *o, *o_sh;
   uint16_t *dec_h;  // decode-shape calls only
   float *logits;    // [T][E]: router logits of moe_layer_forward_router when they go through memory
+  uint8_t *ids8;    // [T*k]: the top-k ids as bytes, for the scatter's count (E <= 256)
 };
 
 // Layout of the layer workspace for T tokens (base == nullptr: size only).
@@ -217,6 +218,7 @@ size_t carve_layer(int T, const moe_layer_t *L, char *base, Workspace *w,
   } else {
     o.dec_h = nullptr;
   }
+  o.ids8 = c.take<uint8_t>((size_t)round_up(tk, 16));
   if (w) *w = o;
   if (lay) *lay = ofs;
   return (size_t)round_up((int64_t)c.off, kAlign);
@@ -232,14 +234,20 @@ size_t layer_ws_bytes(int T, const moe_layer_t *L) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 int enqueue_scan(int T, int E, int k, const moe_routing_t &rt, int32_t *chunk_counts, int32_t *units,
-                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows);
+                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows, const uint8_t *ids8 = nullptr);
+
+// The byte copy of the ids is used when every id fits a byte and the pairs
+// come in whole 16-byte groups.
+bool use_ids8(int T, int E, int k, const uint8_t *ids8) {
+  return ids8 != nullptr && E <= 256 && ((int64_t)T * k) % 16 == 0;
+}
 
 int record(hipEvent_t *ev, int i, hipStream_t s);
 
 int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t &rt,
                   int32_t *chunk_counts, int32_t *units, int32_t *num_units, const uint16_t *x,
                   uint16_t *x16, int d, hipStream_t s, hipEvent_t *ev = nullptr, int unit_rows = kUnitRows,
-                  uint32_t *overflow = nullptr) {
+                  uint32_t *overflow = nullptr, uint8_t *ids8 = nullptr) {
   hipError_t err;
   TopkArgs ta{};
   ta.overflow = overflow;
@@ -252,15 +260,17 @@ int enqueue_route(const float *logits, int T, int E, int k, const moe_routing_t 
   ta.x = x;
   ta.x16 = x16;
   ta.d = d;
+  ta.ids8 = use_ids8(T, E, k, ids8) ? ids8 : nullptr;
   err = launch_topk(ta, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
   if (err != hipSuccess) return MOE_EHIP;
-  return enqueue_scan(T, E, k, rt, chunk_counts, units, num_units, s, ev, unit_rows);
+  return enqueue_scan(T, E, k, rt, chunk_counts, units, num_units, s, ev, unit_rows, ta.ids8);
 }
 
 // Histogram, scan, stable scatter, block map and work list from rt.topk_ids.
 int enqueue_scan(int T, int E, int k, const moe_routing_t &rt, int32_t *chunk_counts, int32_t *units,
-                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows) {
+                 int32_t *num_units, hipStream_t s, hipEvent_t *ev, int unit_rows, const uint8_t *ids8) {
   ScanArgs sa{};
+  sa.ids8 = use_ids8(T, E, k, ids8) ? ids8 : nullptr;
   sa.T = T;
   sa.E = E;
   sa.k = k;
@@ -479,7 +489,7 @@ int forward_one(const moe_layer_t *L, const uint16_t *x, const float *logits, in
     if (st == MOE_OK) st = host_route(T, E, k, opt.unit_rows, rt, w.units, w.num_units, s);
   } else {
     st = enqueue_route(logits, T, E, k, rt, w.chunk_counts, w.units, w.num_units, x, w.x16, d, s, ev, opt.unit_rows,
-                       overflow);
+                       overflow, w.ids8);
   }
   if (st != MOE_OK) return st;
 

@@ -73,6 +73,7 @@ struct TopkArgs {
   uint16_t *x16;            // fp16 [T][d], each 8-element run stored as 0,4,1,5,2,6,3,7
   int d;
   uint32_t *overflow;       // nullable: MOE_OVERFLOW_X when an x16 value is not finite
+  uint8_t *ids8;            // nullable: topk_ids again, one byte each (E <= 256)
   int topk_wgs;             // set by launch_topk: workgroups [0, topk_wgs) route, the rest convert x
 };
 
@@ -98,6 +99,7 @@ struct ScanArgs {
   int32_t *chunk_counts;        // scratch [ceil(T/64)][E] (two-pass form only)
   int count_inline;             // set by launch_scan: the scatter workgroups count every pair themselves
   int ids_vec;                  // set by launch_scan: topk_ids 16-byte aligned and T*k a multiple of 4
+  const uint8_t *ids8;          // nullable: byte copy of topk_ids (E <= 256, 16-byte aligned, T*k % 16 == 0)
 };
 
 // logits[t][e] = sum_k x[t][k] * w[e][k] (bf16 inputs, fp32 accumulation).

@@ -62,6 +62,7 @@ __device__ void route_token(const TopkArgs &a, int t, int lane) {
     a.topk_ids[(int64_t)t * a.k + lane] = id;
     a.topk_w[(int64_t)t * a.k + lane] = g;
   }
+  if (a.ids8 && lane < a.k) a.ids8[(int64_t)t * a.k + lane] = (uint8_t)id;  // the scatter's count reads these
 }
 
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t two_bf16) {
@@ -247,6 +248,30 @@ __device__ __forceinline__ void count_ids4(const int32_t *ids, int64_t n4, int64
   }
 }
 
+// Histogram of n16 groups of sixteen byte ids (16-byte loads, KB per thread
+// in flight): groups below lo16 into pre, the others into post.
+template <int KB>
+__device__ __forceinline__ void count_ids16(const uint8_t *ids, int n16, int lo16, int *pre, int *post) {
+  const uint4 *ids16 = reinterpret_cast<const uint4 *>(ids);
+  for (int b0 = threadIdx.x; b0 < n16; b0 += KB * kThreads) {
+    uint4 v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) v[u] = ids16[min(b0 + u * kThreads, n16 - 1)];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int i16 = b0 + u * kThreads;
+      if (i16 < n16) {
+        int *h = i16 < lo16 ? pre : post;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) atomicAdd(&h[(w[q] >> (8 * b)) & 0xFFu], 1);
+      }
+    }
+  }
+}
+
 // GEMM work list (one workgroup): each expert's rows split into
 // ceil(rows / unit_rows) units whose sizes differ by at most one, listed by 16-row size class, largest first,
 // so the GEMM (which hands units to workgroups in list order) starts the
@@ -382,7 +407,12 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScanArgs a) {
       s_mask[e] = 0ull;
     }
     __syncthreads();
-    if (a.ids_vec && tk > 16 * kThreads) {
+    if (a.ids8) {
+      // byte ids (E <= 256): sixteen per 16-byte load, a quarter of the
+      // bytes every workgroup reads (lo is a multiple of 64 k, so a group of
+      // sixteen falls on one side of it)
+      count_ids16<4>(a.ids8, tk >> 4, lo >> 4, s_pre, s_aux);
+    } else if (a.ids_vec && tk > 16 * kThreads) {
       // more than 4096 pairs, 16-byte aligned ids, T*k a multiple of 4: four
       // ids per load, sixteen loads per thread in flight (lo is a multiple
       // of 64, so the four ids of a load fall on one side of it); up to 4096
