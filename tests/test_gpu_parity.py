@@ -268,6 +268,22 @@ def test_layer_all_tokens_one_expert_set(moe):
     check_output(y, O.moe_forward(p.layer, p.x, p.logits, 2), "dense special case")
 
 
+@pytest.mark.timeout(300)
+def test_layer_max_call_tokens(moe):
+    """One moe_layer_forward call at the per-call maximum, T = 16384 tokens of
+    the Qwen-shaped layer (131072 pairs: the count pass, work lists of
+    thousands of units): routing bit-exact, and every 256th output row
+    against the oracle (each token's output depends only on its own row)."""
+    T = 16384  # MOE_MAX_CALL_TOKENS in include/moe_int4.h
+    shape = S.LayerShape(d=2048, f=512, E=256, k=8, f_sh=512)
+    p = S.make_custom(T, shape, seed=16384)
+    say(f"layer at the call maximum T={T}")
+    y, routing = run_layer(moe, p)
+    check_routing(routing, O.route(p.logits, shape.k), T, shape.k)
+    rows = np.arange(0, T, 256)
+    check_output(y[rows], O.moe_forward(p.layer, p.x[rows], p.logits[rows], shape.k), f"T={T}, {len(rows)} rows")
+
+
 @pytest.mark.parametrize("index", [1, 2])
 def test_layer_bit_reproducible(moe, index):
     """Repeated calls on the same inputs give the same y bit for bit (every
