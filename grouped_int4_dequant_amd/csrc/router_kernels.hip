@@ -6,17 +6,19 @@
 // v_mfma_f32_16x16x32_bf16 in a fixed order (32 inputs per MFMA, ascending),
 // so repeated calls give identical logits. A workgroup of four waves covers
 // 32 tokens x 64 experts; a wave owns 16 experts and both 16-row blocks.
-// The token rows are shared by the four waves, so they pass through LDS once
-// per workgroup in chunks of 256 inputs (double buffered, 16-byte units
-// XOR-swizzled by row so the 16 rows read by one MFMA operand fetch hit
-// distinct banks); each wave reads its experts' weights straight from
-// memory, requesting the next chunk's before computing the current one. The
-// chunk loop body has no per-step branch (columns past d are staged as
-// zeros, which add exactly zero to accumulators that start at +0, and the
-// chunk count is rounded up to the unroll of two), so the compiler keeps the
-// next chunk's loads in flight across iterations. Calls of at most 16 tokens
-// take a second form (router_small_kernel below) that spreads W_r over four
-// times as many workgroups.
+// Both operands pass through LDS in chunks of 256 inputs (double buffered,
+// 16-byte units XOR-swizzled by row so the 16 rows read by one MFMA operand
+// fetch hit distinct banks): the 32 token rows, shared by the four waves, and
+// the 64 expert rows, so every request is a coalesced 512-byte row segment
+// (each wave reading its own experts' rows straight from memory, 16 segments
+// of 64 bytes per request, took 11.6 against 10.0 us at T=2048 for the same
+// logits bit for bit). The next chunk is requested before the current one is
+// computed. The chunk loop body has no per-step branch (columns past d are
+// staged as zeros, which add exactly zero to accumulators that start at +0,
+// and the chunk count is rounded up to the unroll of two), so the compiler
+// keeps the next chunk's loads in flight across iterations. Calls of at most
+// 16 tokens take a second form (router_small_kernel below) that spreads W_r
+// over four times as many workgroups.
 
 // Pages cited (titles as published):
 //   Lily-EN  "Perplexity Open Sources Lily: A Rust + Metal Inference Engine
@@ -37,84 +39,90 @@ constexpr int kChunkSteps = 8;      // 32-input steps per LDS chunk (256 inputs)
 constexpr int kRowBytes = kChunkSteps * 64;  // one token row of a chunk (bf16)
 
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kRouterRows * kRowBytes];  // 2 x 16 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kRouterRows * kRowBytes];     // 2 x 16 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kRouterExperts * kRowBytes];  // 2 x 32 KiB
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * kRouterRows;
-  const int e = blockIdx.y * kRouterExperts + wave * 16 + c16;
-  // experts past the end read the last valid one (never stored)
-  const int ec = min(e, a.E - 1);
-  const uint4 *wr = reinterpret_cast<const uint4 *>(a.w + (int64_t)ec * a.d) + kq;
-  const int steps = a.d / 32;                             // this lane's 16-byte chunk of step s is 4 s + kq
+  const int e0 = blockIdx.y * kRouterExperts;
+  const int e = e0 + wave * 16 + c16;
+  const int steps = a.d / 32;
   // chunks rounded up to an even count: the loop body is straight-line code
   // (no per-step branch), so the compiler keeps the next chunk's loads in
-  // flight across the loop; columns past d are staged as zeros, which add
-  // exactly zero to accumulators that start at +0
+  // flight across the loop; columns past d are staged as zeros in x, which
+  // add exactly zero to accumulators that start at +0
   const int nchunks = 2 * ((steps + 2 * kChunkSteps - 1) / (2 * kChunkSteps));
-
-  // token-row staging: unit u = tid + 256 i of a chunk is row u / 32, 16-byte
-  // column u % 32 (rows past T repeat the last token; columns past d are not
-  // read back)
-  static_assert(kRouterRows * (kRowBytes / 16) == 4 * 256, "four 16-byte units per thread and chunk");
+  // staging: unit u = tid + 256 i of a chunk is row u / 32 (a token of the
+  // block, or an expert of the block), 16-byte column u % 32; rows past T or
+  // E repeat the last one, columns past d are clamped (never used: x is zero
+  // there)
+  static_assert(kRouterRows * (kRowBytes / 16) == 4 * 256, "four 16-byte x units per thread and chunk");
+  static_assert(kRouterExperts * (kRowBytes / 16) == 8 * 256, "eight 16-byte weight units per thread and chunk");
   auto x_src = [&](int c, int i) {
     const int u = tid + 256 * i, r = u >> 5, j = u & 31;
     const int tr = min(t0 + r, a.T - 1);
-    const int col = min(c * kChunkSteps * 32 + 8 * j, a.d - 8);  // clamped, never read back past d
+    const int col = min(c * kChunkSteps * 32 + 8 * j, a.d - 8);
     return reinterpret_cast<const uint4 *>(a.x + (int64_t)tr * a.d + col);
   };
   auto x_dst = [&](int buf, int i) {
     const int u = tid + 256 * i, r = u >> 5, j = u & 31;
     return reinterpret_cast<uint4 *>(&s_x[buf][r * kRowBytes + 16 * (j ^ (r & 15))]);
   };
-  // this thread's four units of the next chunk (compiler vector type: a
-  // select of the struct form costs about 40 more registers)
-  u4 xr[4];
+  auto w_src = [&](int c, int i) {
+    const int u = tid + 256 * i, r = u >> 5, j = u & 31;
+    const int er = min(e0 + r, a.E - 1);
+    const int col = min(c * kChunkSteps * 32 + 8 * j, a.d - 8);
+    return reinterpret_cast<const uint4 *>(a.w + (int64_t)er * a.d + col);
+  };
+  auto w_dst = [&](int buf, int i) {
+    const int u = tid + 256 * i, r = u >> 5, j = u & 31;
+    return reinterpret_cast<uint4 *>(&s_w[buf][r * kRowBytes + 16 * (j ^ (r & 15))]);
+  };
+  // this thread's units of the next chunk (compiler vector type: a select
+  // of the struct form costs about 40 more registers)
+  u4 xr[4], wreg[8];
   auto live = [&](int c, int i) { return c * kChunkSteps * 32 + 8 * ((tid + 256 * i) & 31) < a.d; };
-  auto load_x = [&](int c) {
+  auto load = [&](int c) {
     u4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u4 *>(x_src(c, i));
 #pragma unroll
+    for (int i = 0; i < 8; ++i) wreg[i] = *reinterpret_cast<const u4 *>(w_src(c, i));
+#pragma unroll
     for (int i = 0; i < 4; ++i) xr[i] = live(c, i) ? v[i] : u4{0u, 0u, 0u, 0u};
   };
-  auto store_x = [&](int buf) {
+  auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u4 *>(x_dst(buf, i)) = xr[i];
-  };
-  typedef uint4 WChunk[kChunkSteps];
-  auto load_w = [&](WChunk &cw, int c) {
 #pragma unroll
-    for (int u = 0; u < kChunkSteps; ++u) cw[u] = wr[4 * min(c * kChunkSteps + u, steps - 1)];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u4 *>(w_dst(buf, i)) = wreg[i];
   };
-
   f4 acc0 = f4{0.f, 0.f, 0.f, 0.f}, acc1 = f4{0.f, 0.f, 0.f, 0.f};
+  const int wrow = 16 * wave + c16;  // this lane's expert row of the weight tile
   // One chunk: the barrier publishes chunk c in LDS and frees the other
-  // buffer; chunk c+1's rows and weights are requested (the last chunk
-  // requests itself again), chunk c is computed, then c+1's rows go to LDS.
-  auto body = [&](int c, const WChunk &w, WChunk &wn) {
+  // buffers; chunk c+1's rows and weights are requested (the last chunk
+  // requests itself again), chunk c is computed, then c+1 goes to LDS.
+  auto body = [&](int c) {
     __syncthreads();
-    const int cn = min(c + 1, nchunks - 1);
-    load_x(cn);
-    load_w(wn, cn);
+    load(min(c + 1, nchunks - 1));
     const uint8_t *xb = s_x[c & 1];
+    const uint8_t *wb = s_w[c & 1] + wrow * kRowBytes;
 #pragma unroll
     for (int u = 0; u < kChunkSteps; ++u) {
       const int j = 4 * u + kq;
-      const bf8 wv = __builtin_bit_cast(bf8, w[u]);
+      const uint4 wv = *reinterpret_cast<const uint4 *>(wb + 16 * (j ^ c16));
       const uint4 xa = *reinterpret_cast<const uint4 *>(xb + c16 * kRowBytes + 16 * (j ^ c16));
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), wv, acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xa), __builtin_bit_cast(bf8, wv), acc0, 0, 0, 0);
       const uint4 xc = *reinterpret_cast<const uint4 *>(xb + (16 + c16) * kRowBytes + 16 * (j ^ c16));
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), wv, acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xc), __builtin_bit_cast(bf8, wv), acc1, 0, 0, 0);
     }
-    store_x((c + 1) & 1);
+    store((c + 1) & 1);
   };
-  WChunk w0, w1;
-  load_x(0);
-  load_w(w0, 0);
-  store_x(0);
+  load(0);
+  store(0);
   for (int c = 0; c < nchunks; c += 2) {
-    body(c, w0, w1);
-    body(c + 1, w1, w0);
+    body(c);
+    body(c + 1);
   }
   // element i of lane (c16, kq): token row 4 kq + i of the block, expert c16
   if (e < a.E) {
