@@ -78,7 +78,8 @@ __device__ __forceinline__ uint4 x_chunk_h8(uint4 v) {
   return __builtin_bit_cast(uint4, rb_perm8(xf));
 }
 
-// ONE: calls of one token (T == 1), whose k picks are the distinct experts.
+// ONE: calls of one token (T == 1) at d <= 2048, whose k picks are the
+// distinct experts; their code requests are staged through LDS (below).
 // Several tokens with up to 512 experts: five waves per SIMD (every T = 4
 // workgroup resident at once); the one-token and 1024-expert forms keep
 // their registers.
@@ -113,6 +114,10 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
   // dynamic LDS: the call's activations, then the waves' partial sums
   extern __shared__ uint4 s_x[];  // [T * d / 8]
   float(*s_red)[2][256] = reinterpret_cast<float(*)[2][256]>(s_x + T * (a.d / 8));  // [waves][2][256]
+  // one token (at most four waves): then each wave's codes on their way into
+  // the MFMA layout, [waves][gate/up][16 rows][16 units], units XOR-swizzled
+  // by row
+  uint4(*s_wst)[2][16][16] = reinterpret_cast<uint4(*)[2][16][16]>(s_red + nthreads / 64);
   uint4 xr0 = make_uint4(0u, 0u, 0u, 0u);
   if (x_one) xr0 = reinterpret_cast<const uint4 *>(a.x)[pt * nthreads + tid];  // nthreads = d / 8
 
@@ -201,12 +206,34 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
   const int kbase = wave * kSpan, nwaves = nthreads / 64;
 
   // ---- requests: codes, scales/biases, activations (all before any use)
+  // One token: each wave's 16 rows x 256 bytes of codes per projection come
+  // in four whole 1 KiB requests (lane l: row 4 s + l / 16 of the 16, 16-byte
+  // unit l % 16 of the row's 256 bytes) and pass through LDS into the MFMA
+  // layout below; requests of 16 row segments of 64 bytes each, straight in
+  // that layout, took a third more L1 work. Several tokens keep the direct
+  // form (the staging's LDS would cost T = 4 its residency); one token with
+  // more than four waves (d > 2048), whose staging would pass 64 KiB of LDS,
+  // runs as the pair form.
   u4v code[2][kSteps], sw[2], bw[2];
+  const int lr = lane >> 4, lu = lane & 15;
+  if constexpr (ONE) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int grow = (cb == 0 ? 0 : fe) + 16 * hc + 4 * s + lr;
+        code[cb][s] = *reinterpret_cast<const u4v *>(wq + (int64_t)grow * (d / 8) + kbase / 8 + 4 * lu);
+      }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint32_t *cr = wq + (int64_t)row[cb] * (d / 8) + (kbase + 32 * kq) / 8;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) code[cb][s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
+    }
+  }
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const uint32_t *cr = wq + (int64_t)row[cb] * (d / 8) + (kbase + 32 * kq) / 8;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) code[cb][s] = *reinterpret_cast<const u4v *>(cr + 16 * s);
     sw[cb] = *reinterpret_cast<const u4v *>(wsc + (int64_t)row[cb] * G + kbase / 64);
     bw[cb] = *reinterpret_cast<const u4v *>(wbi + (int64_t)row[cb] * G + kbase / 64);
   }
@@ -238,7 +265,25 @@ __global__ __launch_bounds__(kMaxWaves * 64, (!ONE && VPL <= 8) ? 5 : 1) void de
                                         f16x2_nonfinite(h8.w), MOE_OVERFLOW_X);
       }
   }
+  if constexpr (ONE) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int r16 = 4 * s + lr;
+        s_wst[wave][cb][r16][lu ^ r16] = make_uint4(code[cb][s][0], code[cb][s][1], code[cb][s][2], code[cb][s][3]);
+      }
+  }
   __syncthreads();
+  if constexpr (ONE) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const uint4 v = s_wst[wave][cb][c16][(4 * s + kq) ^ c16];
+        code[cb][s] = u4v{v.x, v.y, v.z, v.w};
+      }
+  }
   const int tok = nth_bit(mask, c16 < nrows ? c16 : 0);
   const uint4 *xl = s_x + ((int64_t)tok * d + kbase + 32 * kq) / 8;
 
@@ -446,9 +491,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s, hipEvent_t gu_start
                          hipEvent_t dn_stop) {
   const int vpl = (a.E + 63) / 64;
   const dim3 g1((a.T * a.k + 1) * (a.fmax / 16)), b1(64 * (a.d / kSpan));
-  // the call's activations, then each wave's partial sums (2 x 256 floats)
-  const size_t xlds = (size_t)a.T * a.d * 2 + (size_t)(a.d / kSpan) * 2 * 256 * sizeof(float);
-  if (a.T == 1)                     launch_decode_gu<true, false>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
+  // the call's activations, then each wave's partial sums (2 x 256 floats);
+  // the one-token form (at most four waves): then each wave's staged codes
+  // (2 x 16 x 256 bytes)
+  const bool one = a.T == 1 && a.d / kSpan <= 4;
+  const size_t xlds = (size_t)a.T * a.d * 2 + (size_t)(a.d / kSpan) * 2 * 256 * sizeof(float) +
+                      (one ? (size_t)(a.d / kSpan) * 2 * 16 * 256 : 0);
+  if (one)                          launch_decode_gu<true, false>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
   else if (a.T <= kDecodePairMaxT)  launch_decode_gu<false, true>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
   else                              launch_decode_gu<false, false>(a, vpl, g1, b1, xlds, s, gu_start, gu_stop);
   hipError_t err = hipGetLastError();
