@@ -140,39 +140,62 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // waves, each requesting its x and W_r operands eight steps at a time before
 // the first MFMA. W_r is then streamed by E / 16 workgroups instead of the
 // E / 64 of the block form, whose four-wave workgroups each pull 256 KiB
-// through one CU. The waves' partial sums meet in LDS and are added in wave
-// order, so repeated calls give identical logits.
+// through one CU. W_r comes in whole 512-byte row segments through a
+// per-wave LDS tile (16 row segments of 64 bytes per request, straight in the
+// MFMA layout, took 3.9 against 3.0 us per T = 1 call); the token rows are
+// read directly (staging them too was slower at T = 1 and 4). The waves'
+// partial sums meet in LDS and are added in wave order, so repeated calls
+// give identical logits.
 constexpr int kSmallRows = 16;   // tokens of the one row block
 constexpr int kSmallWaves = 8;   // input slices per workgroup
 constexpr int kSmallBatch = 8;   // 32-input steps requested at once
 __global__ __launch_bounds__(64 * kSmallWaves) void router_small_kernel(RouterArgs a) {
   __shared__ f4 s_part[kSmallWaves][64];
+  // each wave's W_r batch on its way into the MFMA layout: 16 expert rows x
+  // 32 16-byte units (eight 32-input steps), units XOR-swizzled by row
+  __shared__ u4 s_ws[kSmallWaves][16][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int e = blockIdx.x * 16 + c16;
-  // experts past the end read the last valid one, token rows past T the
-  // last token (neither is stored)
-  const int ec = min(e, a.E - 1), tr = min(c16, a.T - 1);
+  // token rows past T read the last token, expert rows past E the last
+  // expert (neither is stored)
+  const int tr = min(c16, a.T - 1);
   const int steps = a.d / 32;
   const int s0 = wave * steps / kSmallWaves, s1 = (wave + 1) * steps / kSmallWaves;
   // lane (c16, kq): A row c16 (a token) and B column c16 (an expert), inputs
   // 32 s + 8 kq .. + 7 of step s
   const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (int64_t)tr * a.d) + kq;
-  const uint4 *wr = reinterpret_cast<const uint4 *>(a.w + (int64_t)ec * a.d) + kq;
+  // W_r in whole 512-byte row segments: request u of a batch covers expert
+  // rows 2 u and 2 u + 1 of the 16 (lane l: row 2 u + l / 32, unit l % 32 =
+  // step (l % 32) / 4 of the batch, 16-byte quarter l % 4)
+  const int wl = lane >> 5, wu = lane & 31;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   for (int sb = s0; sb < s1; sb += kSmallBatch) {
-    uint4 xv[kSmallBatch], wv[kSmallBatch];
+    uint4 xv[kSmallBatch];
+    u4 wraw[kSmallBatch];
+    const int stu = min(sb + (wu >> 2), s1 - 1);
 #pragma unroll
     for (int u = 0; u < kSmallBatch; ++u) {
       const int st = min(sb + u, s1 - 1);
       xv[u] = xr[4 * st];
-      wv[u] = wr[4 * st];
+      const int er = min((int)blockIdx.x * 16 + 2 * u + wl, a.E - 1);
+      wraw[u] = reinterpret_cast<const u4 *>(a.w + (int64_t)er * a.d)[4 * stu + (wu & 3)];
     }
+    // the previous batch's reads of s_ws are done before it is overwritten,
+    // and these writes before the reads below (one wave's LDS operations
+    // run in order; the fences keep the compiler from moving them)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u) s_ws[wave][2 * u + wl][wu ^ (2 * u + wl)] = wraw[u];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
     for (int u = 0; u < kSmallBatch; ++u)
-      if (sb + u < s1)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xv[u]), __builtin_bit_cast(bf8, wv[u]),
-                                                      acc, 0, 0, 0);
+      if (sb + u < s1) {
+        const u4 wv = s_ws[wave][c16][(4 * u + kq) ^ c16];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, xv[u]), __builtin_bit_cast(bf8, wv), acc,
+                                                      0, 0, 0);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
   s_part[wave][lane] = acc;
   __syncthreads();
