@@ -357,7 +357,7 @@ def bench_prefill_configs(moe, S, torch, dev, steps):
     512-token layer (one moe_layer_forward call) and the 8192-token prompt
     with Zipf-skewed routing (one moe_prefill_chunked call over four
     2048-token chunks). GPU time per call from events around back-to-back
-    calls after a warm-up; weight bytes count each chunk's touched experts
+    calls after 300 ms of untimed calls; weight bytes count each chunk's touched experts
     (from the logits) plus the shared expert, read once per chunk."""
     res = {}
     for ci in (1, 3):
@@ -376,9 +376,13 @@ def bench_prefill_configs(moe, S, torch, dev, steps):
             def call():
                 moe.layer_forward(layer, x, lg, y=y, ws=ws)
         n = max(1, steps if not chunk else steps // 4)
-        for _ in range(5):
-            call()
-        torch.cuda.synchronize()
+        # untimed calls for 300 ms first: building the inputs leaves the GPU
+        # idle for seconds, and its clocks ramp up again only under load
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(n):
