@@ -24,6 +24,10 @@ import os
 import sys
 import time
 
+# kernel arguments in device memory, set before the HIP runtime starts (the
+# package sets the same default on import); reported in the JSON line
+os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
+
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -251,6 +255,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "runtime_env": {"HIP_FORCE_DEV_KERNARG": os.environ.get("HIP_FORCE_DEV_KERNARG")},
         "config": {"workload": "moe_layer_prefill", "T": T, "d": sh.d, "f": sh.f, "E": sh.E, "k": sh.k,
                    "f_sh": sh.f_sh, "weights": "int4 groupwise-affine g=64 bf16 scale+bias",
                    "weights_layout": "prepared" if layer.c.prep else "original",
