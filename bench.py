@@ -49,8 +49,8 @@ TRAFFIC_SOURCES = ("grouped_int4_dequant_amd/csrc/gemm_kernels.hip",
                    "grouped_int4_dequant_amd/csrc/moe_api.hip",
                    "grouped_int4_dequant_amd/csrc/routing_kernels.hip")
 TRAFFIC_DIGEST = "86eceafb1f07be89bdca7edde552d2d73258ab0b420ffdec30bb19f533486c4e"
-TRAFFIC_BYTES = {"gate_up": (185243.7 * 2.0 + 18432.0) * 1024,
-                 "down_combine": (85496.5 * 2.0 + 73728.0 + 37144.5 * 2.0 + 16384.2) * 1024}
+TRAFFIC_BYTES = {"gate_up": (185227.0 * 2.0 + 18432.0) * 1024,
+                 "down_combine": (85494.7 * 2.0 + 73728.0 + 37144.5 * 2.0 + 16385.1) * 1024}
 
 
 def sources_digest():
